@@ -1,0 +1,185 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for causal attention with a sliding
+ * window and a learnable per-head sink.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * What it computes (one query row, one head):
+ *
+ *   Sources (page title, section):
+ *   - "MiMo-V2-Flash Technical Report" digest, 前置知识 / 注意力sink偏置
+ *     (attention-sink bias): every head adds a learnable term s_sink to the
+ *     softmax denominator, i.e. a virtual sink token that can take attention
+ *     mass away from the real tokens.  The virtual token has no value vector
+ *     (it contributes nothing to the numerator).
+ *   - same page, 前置知识 / 混合注意力机制 (hybrid attention) and 核心方法
+ *     (core method): sliding-window layers see only a local window of
+ *     128 tokens; global layers see the whole (causal) prefix.
+ *   - "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？| ICML 2026", §02 of
+ *     the talk: grouped-query attention is used throughout.
+ *
+ *   For query row i of head h (KV head g = h / (Hq/Hkv)), with key set K_i:
+ *     x_j  = (1/sqrt(D)) * sum_d q[i,h,d] * k[j,g,d]           j in K_i
+ *     M    = max(s_h, max_j x_j)
+ *     Z    = sum_j exp(x_j - M)
+ *     E    = exp(s_h - M)            (0 when s_h = -inf)
+ *     out  = sum_j exp(x_j - M) * v[j,g,:] / (Z + E)
+ *     lse  = M + log(Z + E)
+ *   An empty key set leaves only the sink: out = 0, lse = s_h.
+ *
+ * Everything is evaluated directly in double precision from the exact input
+ * values: no tiling, no online rescaling, no reordering.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* Attention of one query row over n key rows given by pointer arrays. */
+static void attend_row(const double *qrow, int64_t D, double sink,
+                       const double *const *krows, const double *const *vrows,
+                       int64_t n, double *x, double *out_row, double *lse_out)
+{
+    const double scale = 1.0 / sqrt((double)D);
+    double M = sink;
+    for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += qrow[d] * krows[j][d];
+        x[j] = scale * dot;
+        if (x[j] > M)
+            M = x[j];
+    }
+    for (int64_t d = 0; d < D; ++d)
+        out_row[d] = 0.0;
+    if (n == 0) {
+        /* Only the virtual sink token is left; it has no value vector. */
+        *lse_out = sink;
+        return;
+    }
+    double Z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        const double w = exp(x[j] - M);
+        Z += w;
+        for (int64_t d = 0; d < D; ++d)
+            out_row[d] += w * vrows[j][d];
+    }
+    const double E = isinf(sink) && sink < 0 ? 0.0 : exp(sink - M);
+    for (int64_t d = 0; d < D; ++d)
+        out_row[d] /= (Z + E);
+    *lse_out = M + log(Z + E);
+}
+
+/*
+ * Query rows r = 0..R-1 of batch qb[r], every head, over the key positions
+ * lo[r]..hi[r] (inclusive; empty when hi < lo) of k/v laid out [B, N, Hkv, D].
+ *   q   [R, Hq, D]     out [R, Hq, D]     lse [R, Hq]     sink [Hq]
+ * Used for sliding-window prefill (lo = max(0, i-W+1), hi = i), for global
+ * causal attention (lo = 0, hi = position of the query) and for sampled rows.
+ */
+void oracle_attend_rows(const double *q, const int64_t *qb, const int64_t *lo,
+                        const int64_t *hi, const double *k, const double *v,
+                        const double *sink, double *out, double *lse,
+                        int64_t R, int64_t N, int64_t Hq, int64_t Hkv, int64_t D)
+{
+    const int64_t G = Hq / Hkv;
+#pragma omp parallel
+    {
+        double *x = NULL;
+        const double **kr = NULL, **vr = NULL;
+        int64_t cap = 0;
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t r = 0; r < R; ++r) {
+            for (int64_t h = 0; h < Hq; ++h) {
+                const int64_t g = h / G;
+                const int64_t first = lo[r] < 0 ? 0 : lo[r];
+                const int64_t last = hi[r] >= N ? N - 1 : hi[r];
+                const int64_t n = last >= first ? last - first + 1 : 0;
+                if (n > cap) {
+                    cap = n;
+                    x = (double *)realloc(x, (size_t)cap * sizeof(double));
+                    kr = (const double **)realloc(kr, (size_t)cap * sizeof(double *));
+                    vr = (const double **)realloc(vr, (size_t)cap * sizeof(double *));
+                }
+                for (int64_t j = 0; j < n; ++j) {
+                    const int64_t pos = first + j;
+                    const int64_t off = ((qb[r] * N + pos) * Hkv + g) * D;
+                    kr[j] = k + off;
+                    vr[j] = v + off;
+                }
+                attend_row(q + (r * Hq + h) * D, D, sink[h], kr, vr, n, x,
+                           out + (r * Hq + h) * D, lse + r * Hq + h);
+            }
+        }
+        free(x);
+        free(kr);
+        free(vr);
+    }
+}
+
+/*
+ * Decode over a fixed ring of W slots per (sequence, KV head): the key of
+ * absolute position P lives in slot P mod W.  Sources: the pwwt.cn article
+ * on MiMo-V2-Flash, §1.1 Hybrid Attention (a sliding-window layer keeps a
+ * fixed-size KV cache, O(W) memory); "小米罗福莉 ... ICML 2026", Q&A on RoPE
+ * (positions keep increasing as the window slides, so cached keys carry
+ * absolute positions); the technical-report digest, 前置知识 / 多token预测
+ * (MTP draft tokens are verified by the main model in one parallel pass).
+ *
+ *   q [B, T, Hq, D]   kc, vc [B, Hkv, W, D]   out [B, T, Hq, D]   lse [B, T, Hq]
+ *   cache_len [B]: L_b = tokens written so far, including the T new ones.
+ * Query t sits at position p = L - T + t and sees the positions
+ * max(0, L-W) .. p: everything older than L-W has been overwritten.
+ */
+void oracle_ring_decode(const double *q, const double *kc, const double *vc,
+                        const double *sink, const int64_t *cache_len,
+                        double *out, double *lse, int64_t B, int64_t T,
+                        int64_t Hq, int64_t Hkv, int64_t W, int64_t D)
+{
+    const int64_t G = Hq / Hkv;
+#pragma omp parallel
+    {
+        double *x = (double *)malloc((size_t)W * sizeof(double));
+        const double **kr = (const double **)malloc((size_t)W * sizeof(double *));
+        const double **vr = (const double **)malloc((size_t)W * sizeof(double *));
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t t = 0; t < T; ++t) {
+                for (int64_t h = 0; h < Hq; ++h) {
+                    const int64_t g = h / G;
+                    const int64_t L = cache_len[b];
+                    const int64_t p = L - T + t;
+                    const int64_t oldest = L - W > 0 ? L - W : 0;
+                    int64_t n = 0;
+                    for (int64_t P = oldest; P <= p; ++P) {
+                        const int64_t slot = P % W;
+                        const int64_t off = ((b * Hkv + g) * W + slot) * D;
+                        kr[n] = kc + off;
+                        vr[n] = vc + off;
+                        ++n;
+                    }
+                    const int64_t row = (b * T + t) * Hq + h;
+                    attend_row(q + row * D, D, sink[h], kr, vr, n, x,
+                               out + row * D, lse + row);
+                }
+            }
+        }
+        free(x);
+        free(kr);
+        free(vr);
+    }
+}
+
+/* Number of (query, key) pairs a causal window-W layer attends over S tokens:
+ * enumerated one row at a time (used to check closed-form FLOP counts). */
+int64_t oracle_count_window_pairs(int64_t S, int64_t W)
+{
+    int64_t total = 0;
+    for (int64_t i = 0; i < S; ++i) {
+        const int64_t lo = i - W + 1 > 0 ? i - W + 1 : 0;
+        total += i - lo + 1;
+    }
+    return total;
+}

@@ -1,0 +1,77 @@
+"""The oracle pins are strong enough to catch plausible mistakes (CPU only).
+
+Each case copies ``oracle/oracle.c``, plants one mistake in the copy (a
+dropped term, a wrong sign, a swapped operand, an off-by-one index), builds
+it in a temporary directory and reruns the pins against it: at least one pin
+must fail.  The real oracle library is restored afterwards.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "lse drops the sink": ("*lse_out = M + log(Z + E);", "*lse_out = M + log(Z);"),
+    "denominator drops the sink": ("out_row[d] /= (Z + E);", "out_row[d] /= Z;"),
+    "sink not shifted by the max": ("exp(sink - M)", "exp(sink)"),
+    "wrong GQA head mapping": ("const int64_t g = h / G;", "const int64_t g = h % Hkv;"),
+    "missing 1/sqrt(D)": ("x[j] = scale * dot;", "x[j] = dot;"),
+    "exponent sign flipped": ("const double w = exp(x[j] - M);",
+                              "const double w = exp(M - x[j]);"),
+    "scores use V": ("dot += qrow[d] * krows[j][d];", "dot += qrow[d] * vrows[j][d];"),
+    "output uses K": ("out_row[d] += w * vrows[j][d];", "out_row[d] += w * krows[j][d];"),
+    "ring slot off by one": ("const int64_t slot = P % W;",
+                             "const int64_t slot = (P + 1) % W;"),
+    "draft position off by one": ("const int64_t p = L - T + t;",
+                                  "const int64_t p = L - T + t - 1;"),
+    "ring keeps one key too few": ("const int64_t oldest = L - W > 0 ? L - W : 0;",
+                                   "const int64_t oldest = L - W + 1 > 0 ? L - W + 1 : 0;"),
+    "pair count misses the diagonal": ("total += i - lo + 1;", "total += i - lo;"),
+}
+
+PINS = [
+    (pins.test_prefill_equals_sdpa_with_virtual_sink_token, dict(W=5)),
+    (pins.test_prefill_equals_sdpa_with_virtual_sink_token, dict(W=100)),
+    (pins.test_sink_neg_inf_is_banded_softmax_attention, {}),
+    (pins.test_window_ge_S_is_full_causal_attention, {}),
+    (pins.test_real_token_mass_is_one_minus_sink_share, {}),
+    (pins.test_single_key_is_logistic, {}),
+    (pins.test_window_locality, {}),
+    (pins.test_gqa_head_mapping, {}),
+    (pins.test_brute_force_decimal, {}),
+    (pins.test_global_bottom_right_causal, {}),
+    (pins.test_ring_decode_equals_sdpa_over_sequence, dict(L=23, T=4)),
+    (pins.test_ring_decode_equals_sdpa_over_sequence, dict(L=9, T=4)),
+    (pins.test_ring_decode_full_ring_matches_prefill_and_is_slot_order_free, {}),
+    (pins.test_ring_decode_draft_windows, {}),
+    (pins.test_window_pair_count_closed_form, dict(S=5000, W=128)),
+]
+
+
+def _build_mutant(tmp_path, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert src.count(old) >= 1, old
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-o", str(lib), str(path), "-lm"], check=True)
+    return oracle.bind(str(lib))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    monkeypatch.setattr(oracle, "_lib", _build_mutant(tmp_path, old, new))
+    caught = []
+    for fn, kw in PINS:
+        try:
+            fn(**kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    assert caught, "no pin caught the planted mistake: %s" % name
