@@ -1,0 +1,147 @@
+/*
+ * swa_sink.h -- C ABI of the MI355X (gfx950) sliding-window + sink attention
+ * library (libswa_sink.so).
+ *
+ * The method (page title, section):
+ *  - "MiMo-V2-Flash Technical Report" digest, 前置知识 / 注意力sink偏置
+ *    (attention-sink bias): each attention head owns a learnable scalar s_h
+ *    that enters the softmax denominator, so attention mass can go to a
+ *    virtual sink token instead of real tokens.  The virtual token carries
+ *    no value vector.
+ *  - same digest, 前置知识 / 混合注意力机制 (hybrid attention) and 核心方法
+ *    (core method): sliding-window layers (window 128) interleaved with
+ *    global full-attention layers at SWA:GA = 5:1.
+ *  - "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？| ICML 2026", §02 of the
+ *    talk: grouped-query attention (GQA) throughout; 7:1 for the larger model.
+ *  - pwwt.cn article on MiMo-V2-Flash, §1.1 Hybrid Attention: the
+ *    sliding-window KV cache has a fixed size, O(W) memory.
+ *
+ * For query row i of head h (KV head g = h / (Hq/Hkv)) with key set K_i:
+ *     x_j = (1/sqrt(D)) q_i . k_j                   (j in K_i)
+ *     out_i = sum_j e^{x_j} v_j / (e^{s_h} + sum_j e^{x_j})
+ *     lse_i = ln(e^{s_h} + sum_j e^{x_j})           (natural log, sink included)
+ * s_h = -inf gives ordinary softmax attention.  An empty key set gives
+ * out = 0, lse = s_h.
+ *
+ * Conventions shared by every call:
+ *  - q, k, v, out and the caches are DEVICE pointers, contiguous, row-major,
+ *    all of element type `dtype` (SWA_F32 or SWA_BF16).  `sink` [Hq] and
+ *    `lse` are always float32 device pointers.  `cache_len` is an int32
+ *    device pointer.
+ *  - The caller owns and allocates every buffer; the library never
+ *    allocates, frees or synchronises, keeps no mutable global state and is
+ *    re-entrant.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and results are valid once the caller synchronises it.
+ *  - Every argument is validated before any HIP call; a non-zero return
+ *    means nothing was launched (SWA_ERR_HIP: the launch itself failed).
+ *    Batch and row counts (B, S, T_q, S_q) may be 0: nothing is launched
+ *    and SWA_OK is returned.
+ *  - Tensor pointers (q, k, v, out, caches, workspace) must be 16-byte
+ *    aligned; sink, lse and cache_len 4-byte aligned (SWA_ERR_UNSUPPORTED).
+ *  - GQA: Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv).
+ *  - Softmax scale is fixed at 1/sqrt(D).
+ *  - Sink values must be finite or -inf (NaN propagates; +inf is undefined).
+ *  - Supported head dims: D in {64, 128}.
+ *  - bfloat16 results are rounded to nearest-even from float32 accumulators.
+ */
+#ifndef SWA_SINK_H
+#define SWA_SINK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SWA_API __attribute__((visibility("default")))
+#else
+#define SWA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum swa_dtype { SWA_F32 = 0, SWA_BF16 = 1 };
+
+enum swa_status {
+    SWA_OK = 0,
+    SWA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    SWA_ERR_SHAPE = -2,       /* negative size, Hq/Hkv/D/window < 1, Hq % Hkv != 0,
+                                 T_q > window, S_q > S_kv, B or Hq > 65535         */
+    SWA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, unknown dtype, misaligned pointer */
+    SWA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
+    SWA_ERR_HIP = -5          /* the HIP runtime reported an error at launch       */
+};
+
+/*
+ * Causal sliding-window prefill with a per-head sink.
+ * Source: technical-report digest, 前置知识 / 混合注意力机制 and
+ * 注意力sink偏置; window 128 per 核心方法.
+ *
+ *   q    [B, S, Hq, D]    k, v [B, S, Hkv, D]    sink [Hq] (float32)
+ *   out  [B, S, Hq, D]    lse  [B, Hq, S] (float32, natural log; may be NULL)
+ * Row i sees key positions max(0, i - window + 1) .. i (window keys,
+ * including itself).  window >= S gives full causal attention.
+ */
+SWA_API int swa_sink_prefill(const void *q, const void *k, const void *v, const float *sink,
+                     void *out, float *lse, int B, int Hq, int Hkv, int S, int D,
+                     int window, int dtype, void *stream);
+
+/*
+ * Decode over a fixed ring KV cache of `window` slots per (sequence, KV head),
+ * with T_q >= 1 new query tokens per sequence (T_q > 1 verifies MTP draft
+ * tokens in one pass).  Sources: pwwt.cn article, §1.1 Hybrid Attention
+ * (fixed-size SWA KV cache); technical-report digest, 前置知识 / 多token预测
+ * (the main model verifies 3 draft tokens in parallel); "小米罗福莉 ...
+ * ICML 2026", Q&A on RoPE (positions keep increasing as the window slides).
+ *
+ *   q       [B, T_q, Hq, D]
+ *   kcache  [B, Hkv, window, D]   the key of absolute position P is in slot P % window
+ *   vcache  [B, Hkv, window, D]
+ *   out     [B, T_q, Hq, D]       lse [B, Hq, T_q] (float32; may be NULL)
+ *   cache_len  int32 [B] on the device: L_b = tokens written so far,
+ *              INCLUDING the T_q new ones (already written to their slots);
+ *              NULL means every ring is exactly full (L = window).
+ * Query t is at position p = L - T_q + t and sees positions max(0, L-window)
+ * .. p (older positions were overwritten).  With a full ring, draft t sees
+ * window - (T_q - 1 - t) keys.  Rows with p < 0 see no key (out = 0).
+ * Requires T_q <= window.  The kernel never reads a slot outside the ring.
+ */
+SWA_API int swa_sink_decode(const void *q, const void *kcache, const void *vcache,
+                    const float *sink, void *out, float *lse, int B, int Hq, int Hkv,
+                    int T_q, int window, int D, const int32_t *cache_len, int dtype,
+                    void *stream);
+
+/*
+ * Workspace (bytes) that global_sink_attn needs for these sizes; 0 means it
+ * needs none (the workspace pointer may then be NULL).  The value does not
+ * depend on dtype.
+ */
+SWA_API size_t global_sink_attn_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
+
+/*
+ * Global (full) causal attention with a per-head sink: the global layers of
+ * the hybrid stack.  Source: technical-report digest, 前置知识 / 混合注意力机制
+ * (global layers see the whole sequence) and 注意力sink偏置.
+ *
+ *   q   [B, S_q, Hq, D]     k, v [B, S_kv, Hkv, D]    sink [Hq]
+ *   out [B, S_q, Hq, D]     lse  [B, Hq, S_q] (float32; may be NULL)
+ * Queries are aligned to the END of the keys: row i sits at position
+ * S_kv - S_q + i and sees keys 0 .. that position (S_q == S_kv is prefill,
+ * S_q << S_kv is decode).  Short query blocks are split over the keys; the
+ * partial results go to `workspace` (device memory of at least
+ * global_sink_attn_workspace_bytes(...) bytes) and a combine pass adds the
+ * sink exactly once.
+ */
+SWA_API int global_sink_attn(const void *q, const void *k, const void *v, const float *sink,
+                     void *out, float *lse, int B, int Hq, int Hkv, int S_q, int S_kv,
+                     int D, void *workspace, size_t workspace_bytes, int dtype,
+                     void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+SWA_API const char *swa_sink_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_SINK_H */

@@ -1,0 +1,144 @@
+"""MI355X-native sliding-window attention with a learnable per-head sink.
+
+Thin Python binding over the C ABI of ``libswa_sink.so`` (hand-written HIP
+kernels for gfx950).  The functions below only marshal arguments: they check
+devices, dtypes and contiguity, allocate outputs with torch (device memory
+plumbing), pass raw pointers plus the current HIP stream, and raise on a
+non-zero status.  Every step of the computation runs in the HIP kernels.
+
+Names follow the C entry points: ``swa_sink_prefill``, ``swa_sink_decode``,
+``global_sink_attn`` (plus ``global_sink_attn_workspace_bytes``).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import SwaError
+
+__all__ = [
+    "swa_sink_prefill",
+    "swa_sink_decode",
+    "global_sink_attn",
+    "global_sink_attn_workspace_bytes",
+    "SwaError",
+]
+
+_DTYPES = {torch.float32: _lib.SWA_F32, torch.bfloat16: _lib.SWA_BF16}
+
+
+def _dtype_code(*tensors) -> int:
+    dt = tensors[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16, got %s" % dt)
+    for t in tensors:
+        if t.dtype != dt:
+            raise TypeError("q, k, v and out must share one dtype")
+    return _DTYPES[dt]
+
+
+def _check_device(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _call(fn, name, *args):
+    rc = fn(*args)
+    if rc != _lib.SWA_OK:
+        raise SwaError(rc, name)
+
+
+def swa_sink_prefill(q, k, v, sink, window: int, out=None, lse=None, want_lse: bool = True,
+                     stream=None):
+    """Causal sliding-window prefill.
+
+    q [B, S, Hq, D], k/v [B, S, Hkv, D] (float32 or bfloat16), sink [Hq] float32.
+    Returns (out [B, S, Hq, D], lse [B, Hq, S] float32 or None).
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch: q %s k %s v %s sink %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(sink.shape)))
+    if sink.dtype != torch.float32:
+        raise TypeError("sink must be float32")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, S), device=q.device, dtype=torch.float32)
+    _check_device(q, k, v, sink, out, lse)
+    dt = _dtype_code(q, k, v, out)
+    _call(_lib.load().swa_sink_prefill, "swa_sink_prefill", _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, int(window), dt, _stream(stream))
+    return out, lse
+
+
+def swa_sink_decode(q, kcache, vcache, sink, cache_len=None, out=None, lse=None,
+                    want_lse: bool = True, stream=None):
+    """Decode T_q tokens per sequence over a W-slot ring cache.
+
+    q [B, T_q, Hq, D]; kcache/vcache [B, Hkv, W, D] (key of position P in slot
+    P % W); cache_len int32 [B] on the GPU (tokens written so far, including
+    the T_q new ones) or None for full rings.  Returns (out, lse [B, Hq, T_q]).
+    """
+    B, T, Hq, D = q.shape
+    Bk, Hkv, W, Dk = kcache.shape
+    if Bk != B or Dk != D or vcache.shape != kcache.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch")
+    if cache_len is not None and (cache_len.dtype != torch.int32 or cache_len.shape != (B,)):
+        raise ValueError("cache_len must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), device=q.device, dtype=torch.float32)
+    _check_device(q, kcache, vcache, sink, out, lse, cache_len)
+    dt = _dtype_code(q, kcache, vcache, out)
+    _call(_lib.load().swa_sink_decode, "swa_sink_decode", _ptr(q), _ptr(kcache), _ptr(vcache),
+          _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, T, W, D, _ptr(cache_len), dt,
+          _stream(stream))
+    return out, lse
+
+
+def global_sink_attn_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D) -> int:
+    return int(_lib.load().global_sink_attn_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D))
+
+
+def global_sink_attn(q, k, v, sink, out=None, lse=None, workspace=None, want_lse: bool = True,
+                     stream=None):
+    """Global causal attention, queries aligned to the end of the keys.
+
+    q [B, S_q, Hq, D], k/v [B, S_kv, Hkv, D]; returns (out, lse [B, Hq, S_q]).
+    ``workspace`` (a uint8 GPU tensor) is allocated when needed and not given.
+    """
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    need = global_sink_attn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_device(q, k, v, sink, out, lse, workspace)
+    dt = _dtype_code(q, k, v, out)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call(_lib.load().global_sink_attn, "global_sink_attn", _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, D, _ptr(workspace), wbytes,
+          dt, _stream(stream))
+    return out, lse

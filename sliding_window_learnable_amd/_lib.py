@@ -1,0 +1,61 @@
+"""ctypes view of libswa_sink.so: the C ABI declared in include/swa_sink.h.
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation anywhere in this package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa_sink.so")
+
+SWA_F32, SWA_BF16 = 0, 1
+SWA_OK = 0
+SWA_ERR_NULL, SWA_ERR_SHAPE, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP = -1, -2, -3, -4, -5
+
+EXPORTS = (
+    "swa_sink_prefill",
+    "swa_sink_decode",
+    "global_sink_attn_workspace_bytes",
+    "global_sink_attn",
+    "swa_sink_strerror",
+)
+
+_lib = None
+
+
+class SwaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (status %d)" % (where, strerror(code), code))
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open the HIP library and declare every exported signature."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            "libswa_sink.so is not built (expected at %s); run "
+            "`python -m sliding_window_learnable_amd.build` or __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.swa_sink_prefill.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp]
+    lib.swa_sink_prefill.restype = i
+    lib.swa_sink_decode.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, i, vp]
+    lib.swa_sink_decode.restype = i
+    lib.global_sink_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.global_sink_attn_workspace_bytes.restype = sz
+    lib.global_sink_attn.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, sz, i, vp]
+    lib.global_sink_attn.restype = i
+    lib.swa_sink_strerror.argtypes = [i]
+    lib.swa_sink_strerror.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().swa_sink_strerror(int(code)).decode()

@@ -1,0 +1,118 @@
+// api.hip -- the extern "C" entry points declared in include/swa_sink.h:
+// argument validation (before any HIP call), dispatch to the kernel
+// launchers, and status codes.
+#include "swa_sink.h"
+
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool dtype_ok(int dtype) { return dtype == SWA_F32 || dtype == SWA_BF16; }
+
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+
+// Grid dimensions y and z carry heads and batch.
+constexpr int kMaxGridYZ = 65535;
+
+int common_checks(int B, int Hq, int Hkv, int D, int dtype) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || D < 1) return SWA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return SWA_ERR_SHAPE;
+    if (B > kMaxGridYZ || Hq > kMaxGridYZ) return SWA_ERR_SHAPE;
+    if (!dtype_ok(dtype) || !head_dim_ok(D)) return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int swa_sink_prefill(const void *q, const void *k, const void *v, const float *sink, void *out,
+                     float *lse, int B, int Hq, int Hkv, int S, int D, int window, int dtype,
+                     void *stream) {
+    if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
+    if (S < 0 || window < 1) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return SWA_OK;
+
+    swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S, S, D, window};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_linear(a, st));
+    if (swa::prefill_ring_supported(window)) return status_of(swa::launch_prefill_ring_bf16(a, st));
+    return status_of(swa::launch_stream_bf16(a, st));
+}
+
+int swa_sink_decode(const void *q, const void *kcache, const void *vcache, const float *sink,
+                    void *out, float *lse, int B, int Hq, int Hkv, int T_q, int window, int D,
+                    const int32_t *cache_len, int dtype, void *stream) {
+    if (!q || !kcache || !vcache || !sink || !out) return SWA_ERR_NULL;
+    if (T_q < 0 || window < 1 || T_q > window) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4) || !aligned(cache_len, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || T_q == 0) return SWA_OK;
+
+    swa::DecodeArgs a{q, kcache, vcache, sink, out, lse, cache_len, B, Hq, Hkv, T_q, window, D};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_ring(a, st));
+    return status_of(swa::launch_ring_decode_bf16(a, st));
+}
+
+size_t global_sink_attn_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_q < 1 || S_kv < S_q || !head_dim_ok(D))
+        return 0;
+    if (!swa::splitkv_preferred(Hq, Hkv, S_q, S_kv)) return 0;
+    return swa::splitkv_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D);
+}
+
+int global_sink_attn(const void *q, const void *k, const void *v, const float *sink, void *out,
+                     float *lse, int B, int Hq, int Hkv, int S_q, int S_kv, int D,
+                     void *workspace, size_t workspace_bytes, int dtype, void *stream) {
+    if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
+    if (S_q < 0 || S_kv < 0 || S_q > S_kv) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S_q == 0) return SWA_OK;
+
+    // Every key position is inside the window: window = S_kv.
+    swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_linear(a, st));
+    if (swa::splitkv_preferred(Hq, Hkv, S_q, S_kv)) {
+        const size_t need = swa::splitkv_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D);
+        if (workspace == nullptr || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SWA_ERR_UNSUPPORTED;
+        return status_of(swa::launch_splitkv_bf16(a, workspace, st));
+    }
+    return status_of(swa::launch_stream_bf16(a, st));
+}
+
+const char *swa_sink_strerror(int code) {
+    switch (code) {
+    case SWA_OK: return "success";
+    case SWA_ERR_NULL: return "a required pointer argument is NULL";
+    case SWA_ERR_SHAPE:
+        return "invalid sizes (negative size, Hq % Hkv != 0, window < 1, T_q > window, "
+               "S_q > S_kv, or batch/heads above 65535)";
+    case SWA_ERR_UNSUPPORTED:
+        return "unsupported argument (head dim not 64/128, unknown dtype, or a pointer "
+               "not aligned to 16 bytes)";
+    case SWA_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case SWA_ERR_HIP: return "the HIP runtime reported an error when launching";
+    default: return "unknown status code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// launch.h -- internal (C++) interface between the C ABI entry points and
+// the kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+struct PrefillArgs {            // also used for global attention
+    const void *q, *k, *v;
+    const float *sink;
+    void *out;
+    float *lse;
+    int B, Hq, Hkv;
+    int S;                      // query rows per sequence (S_q)
+    int S_kv;                   // key rows per sequence
+    int D;
+    int window;                 // keys per row, counting the row itself
+};
+
+struct DecodeArgs {
+    const void *q, *kcache, *vcache;
+    const float *sink;
+    void *out;
+    float *lse;
+    const int32_t *cache_len;   // may be NULL: L = window
+    int B, Hq, Hkv, T, W, D;
+};
+
+// bf16 sliding-window prefill, LDS ring of key tiles (window <= 129).
+bool prefill_ring_supported(int window);
+hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream);
+
+// bf16 banded / causal attention streaming key tiles through LDS: any window,
+// queries aligned to the end of the keys (row i at position S_kv - S + i).
+hipError_t launch_stream_bf16(const PrefillArgs &a, hipStream_t stream);
+
+// bf16 decode over a ring cache (split-free).
+hipError_t launch_ring_decode_bf16(const DecodeArgs &a, hipStream_t stream);
+
+// bf16 split-KV partials over a linear cache + combine (sink added once).
+int splitkv_num_splits(int B, int Hq, int Hkv, int S_q, int S_kv);
+bool splitkv_preferred(int Hq, int Hkv, int S_q, int S_kv);
+size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
+hipError_t launch_splitkv_bf16(const PrefillArgs &a, void *workspace, hipStream_t stream);
+
+// float32 path (one wavefront per query row and head), every call type.
+hipError_t launch_generic_f32_linear(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_generic_f32_ring(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace swa

@@ -18,3 +18,24 @@ def oracle_lib():
 
     oracle._load()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU test on stderr (flushed) before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write("\n[gpu case] %s\n" % request.node.nodeid)
+        sys.stderr.flush()
+    yield
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from sliding_window_learnable_amd import _lib
+
+    _lib.load()          # fails loudly if the HIP library is missing
+    return torch.device("cuda:0")

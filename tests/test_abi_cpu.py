@@ -1,0 +1,145 @@
+"""The C ABI library loads, exports what include/swa_sink.h declares, and
+rejects bad arguments before any HIP call (CPU only, no compute).
+
+Every call here carries at least one invalid argument, so validation must
+return before anything is launched; the pointers are dummies.
+"""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+from sliding_window_learnable_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa_sink.h")
+
+P = 4096          # a 16-byte-aligned dummy address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sliding_window_learnable_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"SWA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = declared_functions()
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, val in [("SWA_OK", 0), ("SWA_ERR_NULL", -1), ("SWA_ERR_SHAPE", -2),
+                      ("SWA_ERR_UNSUPPORTED", -3), ("SWA_ERR_WORKSPACE", -4),
+                      ("SWA_ERR_HIP", -5), ("SWA_F32", 0), ("SWA_BF16", 1)]:
+        assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text), name
+        assert getattr(_lib, name) == val
+
+
+def test_strerror_every_code(lib):
+    seen = set()
+    for code in (0, -1, -2, -3, -4, -5):
+        s = lib.swa_sink_strerror(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.swa_sink_strerror(12345).decode() == "unknown status code"
+
+
+def prefill(lib, q=P, k=P, v=P, sink=P, out=P, lse=None, B=1, Hq=8, Hkv=1, S=16, D=128,
+            window=128, dtype=1):
+    return lib.swa_sink_prefill(q, k, v, sink, out, lse, B, Hq, Hkv, S, D, window, dtype, None)
+
+
+def decode(lib, q=P, kc=P, vc=P, sink=P, out=P, lse=None, B=1, Hq=8, Hkv=1, T=1, W=128, D=128,
+           cache_len=None, dtype=1):
+    return lib.swa_sink_decode(q, kc, vc, sink, out, lse, B, Hq, Hkv, T, W, D, cache_len,
+                               dtype, None)
+
+
+def gattn(lib, q=P, k=P, v=P, sink=P, out=P, lse=None, B=1, Hq=8, Hkv=1, Sq=4, Skv=64, D=128,
+          ws=None, wsb=0, dtype=1):
+    return lib.global_sink_attn(q, k, v, sink, out, lse, B, Hq, Hkv, Sq, Skv, D, ws, wsb,
+                                dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(k=None), _lib.SWA_ERR_NULL),
+    (dict(v=None), _lib.SWA_ERR_NULL), (dict(sink=None), _lib.SWA_ERR_NULL),
+    (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(B=-1), _lib.SWA_ERR_SHAPE), (dict(S=-3), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=0), _lib.SWA_ERR_SHAPE), (dict(Hkv=0), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=8, Hkv=3), _lib.SWA_ERR_SHAPE), (dict(window=0), _lib.SWA_ERR_SHAPE),
+    (dict(D=0), _lib.SWA_ERR_SHAPE), (dict(B=70000), _lib.SWA_ERR_SHAPE),
+    (dict(D=96), _lib.SWA_ERR_UNSUPPORTED), (dict(D=256), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(dtype=2), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=-1), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(q=P + 8), _lib.SWA_ERR_UNSUPPORTED), (dict(out=P + 2), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(lse=P + 2), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def test_empty_inputs_are_noops(lib):
+    # B == 0 or S == 0: nothing to compute, nothing launched, success
+    assert prefill(lib, B=0) == _lib.SWA_OK
+    assert prefill(lib, S=0) == _lib.SWA_OK
+    assert decode(lib, B=0) == _lib.SWA_OK
+    assert decode(lib, T=0) == _lib.SWA_OK
+    assert gattn(lib, Sq=0) == _lib.SWA_OK
+    assert gattn(lib, Sq=0, Skv=0) == _lib.SWA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(kc=None), _lib.SWA_ERR_NULL),
+    (dict(vc=None), _lib.SWA_ERR_NULL), (dict(sink=None), _lib.SWA_ERR_NULL),
+    (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(T=5, W=4), _lib.SWA_ERR_SHAPE), (dict(W=0), _lib.SWA_ERR_SHAPE),
+    (dict(T=-1), _lib.SWA_ERR_SHAPE), (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE),
+    (dict(D=32), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=7), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(cache_len=P + 1), _lib.SWA_ERR_UNSUPPORTED), (dict(kc=P + 4), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(sink=None), _lib.SWA_ERR_NULL),
+    (dict(Sq=65, Skv=64), _lib.SWA_ERR_SHAPE), (dict(Skv=-1), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=5, Hkv=2), _lib.SWA_ERR_SHAPE),
+    (dict(D=100), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=3), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_global_rejects(lib, kw, code):
+    assert gattn(lib, **kw) == code
+
+
+def test_global_workspace_checked(lib):
+    """Decode-shaped global calls split the keys and need a workspace."""
+    need = lib.global_sink_attn_workspace_bytes(8, 64, 8, 1, 262144, 128)
+    assert need > 0
+    assert gattn(lib, B=8, Hq=64, Hkv=8, Sq=1, Skv=262144, ws=None, wsb=0) == _lib.SWA_ERR_WORKSPACE
+    assert gattn(lib, B=8, Hq=64, Hkv=8, Sq=1, Skv=262144, ws=P, wsb=need - 1) == \
+        _lib.SWA_ERR_WORKSPACE
+    # invalid sizes report no workspace
+    assert lib.global_sink_attn_workspace_bytes(8, 64, 8, 5, 4, 128) == 0
+    assert lib.global_sink_attn_workspace_bytes(8, 64, 8, 1, 4096, 96) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import sliding_window_learnable_amd as swa
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        swa.swa_sink_prefill(q, k, k, torch.zeros(8), 128)

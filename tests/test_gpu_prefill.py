@@ -1,0 +1,109 @@
+"""GPU parity: swa_sink_prefill (HIP, through the C ABI) against the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_learnable_amd as swa
+from sliding_window_learnable_amd import inputs
+from tests.parity import check_lse, check_out, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(gpu, cfg, B, S, Hq, Hkv, D, W, dtype, sink_override=None):
+    q, k, v, sink = inputs.attention_inputs(cfg, 0, B, S, S, Hq, Hkv, D, dtype)
+    if sink_override is not None:
+        sink = torch.full((Hq,), float(sink_override))
+    ref_out, ref_lse = oracle.swa_prefill(to64(q), to64(k), to64(v), to64(sink), W)
+    out, lse = swa.swa_sink_prefill(q.to(gpu), k.to(gpu), v.to(gpu), sink.to(gpu), W)
+    torch.cuda.synchronize()
+    check_out(out, ref_out, dtype)
+    check_lse(lse, ref_lse, dtype)
+    return out, lse
+
+
+# --- tiny reference workload (float32): B=1, H=1, S=512, D=64, window 128 ------
+
+@pytest.mark.parametrize("variant", ["sink", "sink=-inf", "window=512"])
+def test_tiny_reference_f32(gpu, variant):
+    W = 512 if variant == "window=512" else 128
+    sink = -np.inf if variant == "sink=-inf" else None
+    run_case(gpu, 1, 1, 512, 1, 1, 64, W, torch.float32, sink)
+
+
+# --- bfloat16 shapes spanning several tiles, ragged tails, GQA group sizes -------
+
+CASES = [
+    # B, S, Hq, Hkv, D, W
+    (2, 300, 8, 1, 128, 128),
+    (1, 257, 16, 2, 64, 128),
+    (1, 1, 8, 8, 128, 128),
+    (1, 70, 4, 4, 128, 1),
+    (2, 100, 6, 2, 128, 33),
+    (1, 200, 16, 1, 128, 129),
+    (1, 131, 8, 4, 64, 32),
+    (3, 97, 4, 2, 128, 31),
+    (1, 1000, 64, 8, 128, 128),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,W", CASES)
+def test_bf16_against_oracle(gpu, B, S, Hq, Hkv, D, W):
+    run_case(gpu, 90, B, S, Hq, Hkv, D, W, torch.bfloat16)
+
+
+def test_bf16_sink_neg_inf(gpu):
+    run_case(gpu, 91, 1, 300, 8, 1, 128, 128, torch.bfloat16, -np.inf)
+
+
+def test_f32_gqa_and_d128(gpu):
+    run_case(gpu, 92, 2, 150, 6, 2, 128, 40, torch.float32)
+
+
+def test_deterministic(gpu):
+    q, k, v, sink = inputs.attention_inputs(93, 0, 1, 700, 700, 16, 2, 128, torch.bfloat16, "cuda")
+    o1, l1 = swa.swa_sink_prefill(q, k, v, sink, 128)
+    o2, l2 = swa.swa_sink_prefill(q, k, v, sink, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --- the 32K prefill workload at full size, checked on sampled rows -------------
+
+def sample_rows(S, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(256, S))) | set(range(max(0, S - 256), S))
+    rows |= set(rng.integers(0, S, n_random).tolist())
+    return np.array(sorted(rows))
+
+
+def test_prefill_32k_sampled_rows(gpu):
+    B, S, Hq, Hkv, D, W = 1, 32768, 64, 8, 128, 128
+    q, k, v, sink = inputs.attention_inputs(2, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out, lse = swa.swa_sink_prefill(q, k, v, sink, W)
+    torch.cuda.synchronize()
+    rows = sample_rows(S, 4096, 2)
+    idx = torch.as_tensor(rows, device=gpu)
+    ref_out, ref_lse = oracle.swa_prefill_rows(
+        to64(q[0].index_select(0, idx)), np.zeros(len(rows)), rows, to64(k), to64(v),
+        to64(sink), W)
+    check_out(out[0].index_select(0, idx), ref_out, torch.bfloat16)
+    check_lse(lse[0].index_select(1, idx).T, ref_lse, torch.bfloat16)
+
+
+def test_prefill_32k_real_token_mass_identity(gpu):
+    """With v == 1 every output element equals the real-token attention mass
+    1 - exp(s_h - lse): checked on every row of the full-size workload."""
+    B, S, Hq, Hkv, D, W = 1, 32768, 64, 8, 128, 128
+    q, k, _, sink = inputs.attention_inputs(2, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    v = torch.ones_like(k)
+    out, lse = swa.swa_sink_prefill(q, k, v, sink, W)
+    torch.cuda.synchronize()
+    mass = 1.0 - torch.exp(sink.double()[None, :, None] - lse.double())       # B Hq S
+    expect = mass.permute(0, 2, 1)[..., None].expand(B, S, Hq, D)
+    err = (out.double() - expect).abs()
+    assert bool((err <= 2e-2 + 1e-2 * expect.abs()).all()), float(err.max())
+    assert bool((mass < 1).all()) and bool((mass > 0).all())
