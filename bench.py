@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliding-window + sink attention hot path on one MI355X.
+
+Headline (one JSON line on stdout): swa_sink_prefill on the 32K prefill
+workload -- B=1, S=32768, Hq=64, Hkv=8, D=128, window 128, bf16 inputs,
+fp32 accumulation, bf16 out + fp32 LSE -- in algorithmic TFLOP/s.  One
+"step" is one prefill call over the whole workload.  Alongside it, in the
+same JSON object:
+  roofline      the prefill kernel against HBM bandwidth (its bound)
+  cpu_baseline  the fp64 oracle timed on the host cores over the same workload
+  decode        ring-cache decode, B=256, 128 slots, T_q = 1 and 4, in HBM GB/s
+  hybrid_5to1   5 SWA layers + 1 global layer at S=65536: per-layer-type time
+  long_context  SWA prefill at S=262144; global decode B=8 over 262144 keys
+Inputs are seeded synthetic Gaussian tensors resident in HBM before timing.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTION]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SWA+sink attention TFLOP/s (prefill, % MFMA peak) and decode HBM GB/s, 1 GPU"
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "sliding_window_learnable_amd", "csrc", "swa_prefill.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "swa_prefill_32k_hbm_traffic.md")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all",
+                    choices=["all", "prefill", "decode", "hybrid", "long", "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` back-to-back calls, timed with
+    HIP events on the stream the kernels are launched on (torch's current
+    stream, which the binding passes to the C ABI)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(i)
+    t1.record(stream)
+    t1.synchronize()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter
+    summary, or None when missing or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    text = open(TRAFFIC_RECORD).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha256(PREFILL_KERNEL_SRC):
+        return None
+    return float(m_b.group(1))
+
+
+# --------------------------------------------------------------------------- sections
+
+def bench_prefill(args, swa, acc, torch):
+    from sliding_window_learnable_amd import inputs
+    B, S, Hq, Hkv, D, W = 1, 32768, 64, 8, 128, 128
+    q, k, v, sink = inputs.attention_inputs(2, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+    log("prefill 32K: warmup %d, steps %d" % (args.warmup, args.steps))
+    ms = timed(lambda i: swa.swa_sink_prefill(q, k, v, sink, W, out=out, lse=lse),
+               args.steps, args.warmup)
+    flops = acc.prefill_flops(B, S, Hq, D, W)
+    nbytes = acc.prefill_bytes(B, S, Hq, Hkv, D)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = dict(ms=ms, tflops=tflops, gbs=gbs, flops=flops, bytes=nbytes,
+               tokens_per_s=B * S / (ms * 1e-3),
+               frac_mfma_peak=tflops / acc.PEAK_BF16_TFLOPS,
+               frac_hbm_peak=gbs / acc.PEAK_HBM_GBS)
+    res["tensors"] = (q, k, v, sink)
+    return res
+
+
+def bench_cpu_baseline(args, acc, torch, tensors):
+    """The fp64 oracle, as it stands, on the host cores: whole passes over the
+    32K prefill workload (every row, every head), repeated until about
+    --cpu-seconds of CPU time has been spent."""
+    import numpy as np
+    import oracle
+    q, k, v, sink = tensors
+    B, S, Hq, D = q.shape
+    W = 128
+    q64 = q.double().cpu().numpy()
+    k64 = k.double().cpu().numpy()
+    v64 = v.double().cpu().numpy()
+    s64 = sink.double().cpu().numpy()
+    t = time.perf_counter()
+    oracle.swa_prefill(q64, k64, v64, s64, W)
+    first = time.perf_counter() - t
+    reps = int(max(1, min(20, round(args.cpu_seconds / max(first, 1e-6)))))
+    log("cpu baseline: one pass %.2fs, %d passes" % (first, reps))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.swa_prefill(q64, k64, v64, s64, W)
+    dt = time.perf_counter() - t
+    flops = reps * acc.prefill_flops(B, S, Hq, D, W)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d full pass(es) of the 32K prefill workload (all 32768 rows, 64 heads), "
+                      "fp64, %.1f s total" % (reps, dt),
+            "seconds": dt}
+
+
+def bench_decode(args, swa, acc, torch):
+    from sliding_window_learnable_amd import inputs
+    B, Hq, Hkv, D, W = 256, 64, 8, 128, 128
+    nsets = 5          # 5 x 128 MiB of ring caches > 256 MiB Infinity Cache
+    res = {"workload": "swa_sink_decode B=256 Hq=64 Hkv=8 D=128 ring=128 bf16, full rings",
+           "cache_rotation": "%d independent input sets (%d MiB of KV) cycled per call"
+                             % (nsets, nsets * 128)}
+    for T in (1, 4):
+        sets = [inputs.ring_inputs(3, layer, B, T, Hq, Hkv, W, D, torch.bfloat16, "cuda")
+                for layer in range(nsets)]
+        outs = [torch.empty_like(s[0]) for s in sets]
+        lses = [torch.empty((B, Hq, T), device="cuda", dtype=torch.float32) for _ in sets]
+
+        def call(i):
+            s = sets[i % nsets]
+            swa.swa_sink_decode(s[0], s[1], s[2], s[3], out=outs[i % nsets], lse=lses[i % nsets])
+
+        steps = max(200, 10 * args.steps)
+        log("decode T_q=%d: %d calls" % (T, steps))
+        ms = timed(call, steps, 20)
+        nbytes = acc.decode_bytes(B, T, Hq, Hkv, W, D)
+        flops = acc.decode_flops(B, T, Hq, D, W)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res["T_q=%d" % T] = dict(us_per_call=ms * 1e3, hbm_gbs=gbs,
+                                 frac_hbm_peak=gbs / acc.PEAK_HBM_GBS,
+                                 tflops=flops / (ms * 1e-3) / 1e12,
+                                 tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes)
+        del sets, outs, lses
+        torch.cuda.empty_cache()
+    res["time_ratio_T4_over_T1"] = res["T_q=4"]["us_per_call"] / res["T_q=1"]["us_per_call"]
+    return res
+
+
+def bench_hybrid(args, swa, acc, torch):
+    """5 SWA+sink layers (window 128) then 1 global causal+sink layer, S=65536."""
+    from sliding_window_learnable_amd import inputs
+    B, S, Hq, Hkv, D, W = 1, 65536, 64, 8, 128, 128
+    layers = [inputs.attention_inputs(4, layer, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+              for layer in range(6)]
+    out = torch.empty_like(layers[0][0])
+    lse = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+
+    def swa_layers(i):
+        for q, k, v, s in layers[:5]:
+            swa.swa_sink_prefill(q, k, v, s, W, out=out, lse=lse)
+
+    def ga_layer(i):
+        q, k, v, s = layers[5]
+        swa.global_sink_attn(q, k, v, s, out=out, lse=lse)
+
+    log("hybrid 5:1 at S=65536")
+    ms_swa5 = timed(swa_layers, 5, 1)
+    ms_ga = timed(ga_layer, 3, 1)
+    f_swa = acc.prefill_flops(B, S, Hq, D, W)
+    f_ga = acc.global_flops(B, S, S, Hq, D)
+    compute_red, kv_red = acc.hybrid_ratios(S, W, 5)
+    del layers
+    torch.cuda.empty_cache()
+    return {
+        "workload": "5 x swa_sink_prefill (window 128) + 1 x global_sink_attn, B=1 S=65536 "
+                    "Hq=64 Hkv=8 D=128 bf16, seeds per layer",
+        "swa_layer_ms": ms_swa5 / 5, "global_layer_ms": ms_ga, "stack_ms": ms_swa5 + ms_ga,
+        "swa_layer_tflops": f_swa / (ms_swa5 / 5 * 1e-3) / 1e12,
+        "global_layer_tflops": f_ga / (ms_ga * 1e-3) / 1e12,
+        "global_layer_frac_mfma_peak": f_ga / (ms_ga * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
+        "swa_layer_hbm_gbs": acc.prefill_bytes(B, S, Hq, Hkv, D) / (ms_swa5 / 5 * 1e-3) / 1e9,
+        "flop_ratio_swa_over_global_per_layer": f_swa / f_ga,
+        "flop_share_of_5_swa_layers": 5 * f_swa / (5 * f_swa + f_ga),
+        "attention_compute_reduction_vs_6_global": compute_red,
+        "kv_cache_reduction_vs_6_global": kv_red,
+        "measured_time_reduction_vs_6_global": 6 * ms_ga / (ms_swa5 + ms_ga),
+    }
+
+
+def bench_long(args, swa, acc, torch):
+    from sliding_window_learnable_amd import inputs
+    res = {}
+    B, S, Hq, Hkv, D, W = 1, 262144, 64, 8, 128, 128
+    q, k, v, sink = inputs.attention_inputs(5, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+    log("long context: SWA prefill S=262144")
+    ms = timed(lambda i: swa.swa_sink_prefill(q, k, v, sink, W, out=out, lse=lse), 5, 2)
+    f = acc.prefill_flops(B, S, Hq, D, W)
+    nb = acc.prefill_bytes(B, S, Hq, Hkv, D)
+    res["swa_prefill_262144"] = dict(ms=ms, tflops=f / (ms * 1e-3) / 1e12,
+                                     hbm_gbs=nb / (ms * 1e-3) / 1e9,
+                                     frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+                                     tokens_per_s=S / (ms * 1e-3))
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+    B, Sq, Skv = 8, 1, 262144
+    q, k, v, sink = inputs.attention_inputs(5, 1, B, Sq, Skv, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), device="cuda", dtype=torch.float32)
+    ws = torch.empty(swa.global_sink_attn_workspace_bytes(B, Hq, Hkv, Sq, Skv, D),
+                     device="cuda", dtype=torch.uint8)
+    log("long context: global decode B=8 over 262144 keys")
+    ms = timed(lambda i: swa.global_sink_attn(q, k, v, sink, out=out, lse=lse, workspace=ws), 20, 3)
+    nb = acc.global_bytes(B, Sq, Skv, Hq, Hkv, D)
+    res["global_decode_B8_262144"] = dict(
+        ms=ms, hbm_gbs=nb / (ms * 1e-3) / 1e9, frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+        tokens_per_s=B / (ms * 1e-3),
+        kv_bytes_per_sequence_vs_swa_ring=Skv / 128)
+    return res
+
+
+def bench_copy(args, torch):
+    """Plain 1 GiB device copy: the reference kernel for scaling PMC byte counters."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda i: dst.copy_(src), 5, 2)
+    return {"bytes_read": n, "bytes_written": n, "ms": ms, "gbs": 2 * n / (ms * 1e-3) / 1e9}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sliding_window_learnable_amd as swa
+    from sliding_window_learnable_amd import _lib
+    from sliding_window_learnable_amd import accounting as acc
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()                              # fails loudly if the HIP library is missing
+
+    if args.only == "copy":
+        print(json.dumps({"copy": bench_copy(args, torch)}))
+        return
+
+    result = {}
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(args, swa, acc, torch)
+        tensors = pre.pop("tensors")
+        traffic = traffic_record()
+        result.update({
+            "metric": METRIC,
+            "value": pre["tflops"],
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": pre["ms"],
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16 q/k/v, N(0,1) fp32 sink)",
+            "config": {"workload": "swa_sink_prefill B=1 S=32768 Hq=64 Hkv=8 D=128 window=128 "
+                                   "bf16 in, fp32 accumulate, bf16 out + fp32 lse",
+                       "B": 1, "S": 32768, "Hq": 64, "Hkv": 8, "D": 128, "window": 128},
+            "prefill": {k: v for k, v in pre.items() if k != "ms"},
+            "roofline": {"bound": "hbm", "achieved": pre["gbs"], "peak": acc.PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": pre["gbs"] / acc.PEAK_HBM_GBS,
+                         "traffic": traffic,
+                         "kernel": "swa_prefill_ring_kernel<128, 8>",
+                         "algorithmic_bytes_per_launch": pre["bytes"]},
+        })
+        if not args.no_cpu_baseline:
+            cb = bench_cpu_baseline(args, acc, torch, tensors)
+            cb["gpu_speedup"] = pre["tflops"] / cb["value"]
+            result["cpu_baseline"] = cb
+        del tensors
+        torch.cuda.empty_cache()
+    if args.only in ("all", "decode"):
+        result["decode"] = bench_decode(args, swa, acc, torch)
+    if args.only in ("all", "hybrid"):
+        result["hybrid_5to1"] = bench_hybrid(args, swa, acc, torch)
+    if args.only in ("all", "long"):
+        result["long_context"] = bench_long(args, swa, acc, torch)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -58,6 +58,8 @@ def bind(path: str):
     lib.oracle_ring_decode.restype = None
     lib.oracle_count_window_pairs.argtypes = [i64, i64]
     lib.oracle_count_window_pairs.restype = i64
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -179,3 +181,8 @@ def count_window_pairs(S: int, W: int) -> int:
     """(query, key) pairs of one causal window-W layer over S tokens, counted
     row by row."""
     return int(_load().oracle_count_window_pairs(int(S), int(W)))
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())

@@ -36,6 +36,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* Attention of one query row over n key rows given by pointer arrays. */
 static void attend_row(const double *qrow, int64_t D, double sink,
@@ -182,4 +185,14 @@ int64_t oracle_count_window_pairs(int64_t S, int64_t W)
         total += i - lo + 1;
     }
     return total;
+}
+
+/* Threads an OpenMP parallel region of the oracle uses. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
