@@ -45,7 +45,7 @@ int swa_sink_prefill(const void *q, const void *k, const void *v, const float *s
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S, S, D, window};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_linear(a, st));
-    if (swa::prefill_ring_supported(window)) return status_of(swa::launch_prefill_ring_bf16(a, st));
+    if (swa::prefill_ring_supported(window, Hq / Hkv)) return status_of(swa::launch_prefill_ring_bf16(a, st));
     return status_of(swa::launch_stream_bf16(a, st));
 }
 

@@ -73,35 +73,50 @@ __device__ __forceinline__ float wave_xor32_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// Work-group barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads and stores (which
+// __syncthreads() would also drain), so prefetches and output stores stay
+// in flight across it.  The memory clobber keeps the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Buffer addressing.  A 128-bit resource (base, byte range) lives in SGPRs,
+// each lane supplies one 32-bit byte offset, uniform offsets go in an SGPR.
+// Loads past the range return zeros and stores past it are dropped, so tile
+// edges need no clamping or branches.  (Word 3 = 0x00020000 is the raw,
+// untyped 32-bit buffer format of the CDNA family.)
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store8(bf16x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store16(bf16x8 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store_f32(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+// A byte offset beyond any range a descriptor here can have: stores to it
+// are dropped, loads from it return zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // Largest power of two dividing G, capped at 8: waves per work-group when
 // one wave serves one query head of a GQA group.
 __host__ __device__ constexpr int waves_for_group(int G) {
     return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
-
-// ---------------------------------------------------------------------------
-// LDS staging of a 32-key tile.
-//
-// K tile : [32 keys][D + 8] bf16 (16-byte row pad: the 8 rows that one
-//          ds_read_b128 quarter-wave touches land on distinct bank groups).
-// V^T    : [D][ring keys + 8] bf16, keys contiguous, so one 16-byte read
-//          gives the 8 consecutive keys of an A operand of O^T = V^T P^T.
-// ---------------------------------------------------------------------------
-
-// Global -> register prefetch of one K chunk (16 bytes) per thread item.
-template <int D>
-struct KChunk {
-    bf16x8 val;
-    int key, chunk;
-    bool live;
-};
-
-// V^T staging item: 4 keys x 8 dims (four 16-byte rows), written to LDS as
-// eight 8-byte stores, one per dim, each holding 4 consecutive keys.
-struct VQuad {
-    bf16x8 rows[4];
-    int kq, chunk;
-    bool live;
-};
 
 }  // namespace swa

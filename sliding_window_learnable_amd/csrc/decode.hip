@@ -49,7 +49,8 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(
     constexpr int NT = 64 * NWD;
     __shared__ __align__(16) DecodeSmem<D> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lq = lane & 31, hl = lane >> 5;
     const int ct = blockIdx.x % n_ct, split = blockIdx.x / n_ct;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(
             }
         }
         if (hl == 0) sm.red_max[wave][lq] = mx;
-        __syncthreads();
+        lds_barrier();
 
         float mc = -INFINITY;
 #pragma unroll
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(
         *(bf16x8 *)&sm.pt[lq][32 * wave + 8 * hl] = pack8(s, 0);
         *(bf16x8 *)&sm.pt[lq][32 * wave + 16 + 8 * hl] = pack8(s, 1);
         if (hl == 0) sm.red_sum[wave][lq] = psum;
-        __syncthreads();
+        lds_barrier();
 
         float lc = 0.0f;
 #pragma unroll
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(
             const bf16x8 pb = *(const bf16x8 *)&sm.pt[lq][16 * k16 + 8 * hl];
             o = mfma32(a, pb, o);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (!col_ok) return;

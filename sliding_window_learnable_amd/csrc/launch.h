@@ -30,7 +30,7 @@ struct DecodeArgs {
 };
 
 // bf16 sliding-window prefill, LDS ring of key tiles (window <= 129).
-bool prefill_ring_supported(int window);
+bool prefill_ring_supported(int window, int G);
 hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream);
 
 // bf16 banded / causal attention streaming key tiles through LDS: any window,

@@ -103,7 +103,8 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     constexpr int NT = NW * 64;
     __shared__ __align__(16) StreamSmem<D> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lq = lane & 31, hl = lane >> 5;
     const int bg = blockIdx.x % BG;
     const int qb = NB - 1 - blockIdx.x / BG;          // longest query blocks first
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     TileLoader<D, NT> ld;
     ld.load(kb, vb, row_stride, S_kv, T_lo, tid);
     ld.store(sm, 0, tid);
-    __syncthreads();
+    lds_barrier();
 
     for (int hh = wave; hh < G; hh += NW) {
         const int h = g * G + hh;
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
                 }
             }
             if (prefetch) ld.store(sm, slot ^ 1, tid);
-            __syncthreads();
+            lds_barrier();
         }
 
         // Sink joins the denominator once: l_total = sum_j e^{x_j - m} + e^{s_h - m}.
@@ -228,10 +229,10 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         }
         if (hh + NW < G) {
             // next head of this wave: restage the first tile
-            __syncthreads();
+            lds_barrier();
             ld.load(kb, vb, row_stride, S_kv, T_lo, tid);
             ld.store(sm, 0, tid);
-            __syncthreads();
+            lds_barrier();
         }
     }
 }

@@ -30,12 +30,18 @@ constexpr int kMaxTiles = 5;             // ceil((129-1)/32) + 1
 constexpr int kRing = kMaxTiles + 1;     // + the tile being prefetched
 constexpr int kRingKeys = kRing * kTile;
 
-template <int D>
+template <int D, int NW>
 struct RingSmem {
     bf16 k[kRing][kTile][D + 8];
     bf16 vt[D][kRingKeys + 8];
+    // Per-wave output staging: 32 queries x 64 dims (half of D = 128 at a
+    // time), so that global stores are whole 128-byte row segments.
+    bf16 ostage[NW][kTile][64 + 4];
 };
 
+// Stages one 32-key tile: K rows as 16-byte chunks into sm.k[slot], V as
+// 4-key x 8-dim quads written transposed into sm.vt.  The global loads go
+// into registers at the start of a step and reach LDS at its end.
 template <int D, int NT>
 struct Stager {
     static constexpr int CH = D / 8;                       // 16-byte chunks per row
@@ -44,37 +50,25 @@ struct Stager {
     bf16x8 kreg[KPT];
     bf16x8 vreg[VPT][4];
 
-    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, size_t row_stride,
-                                         int S, int T, int tid) {
-        bf16x8 z;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    // Rows past the end of the descriptor's range read as zeros.
+    __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, uint32_t rs, uint32_t row0,
+                                         int tid) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int item = tid + i * NT;
-            kreg[i] = z;
-            if (item < kTile * CH) {
-                const int pos = kTile * T + item / CH, ch = item % CH;
-                if (pos < S) kreg[i] = *(const bf16x8 *)(kb + (size_t)pos * row_stride + 8 * ch);
-            }
+            const int item = min(tid + i * NT, kTile * CH - 1);
+            kreg[i] = buf_load16(kr, (item / CH) * rs + 16 * (item % CH), row0 * rs);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
+            const int item = min(tid + i * NT, 8 * CH - 1);
+            const uint32_t vo = 4 * (item & 7) * rs + 16 * (item >> 3);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vreg[i][j] = z;
-            if (item < 8 * CH) {
-                const int kq = item & 7, ch = item >> 3;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int pos = kTile * T + 4 * kq + j;
-                    if (pos < S) vreg[i][j] = *(const bf16x8 *)(vb + (size_t)pos * row_stride + 8 * ch);
-                }
-            }
+            for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, vo, (row0 + j) * rs);
         }
     }
 
-    __device__ __forceinline__ void store(RingSmem<D> &sm, int slot, int tid) const {
+    template <class Smem>
+    __device__ __forceinline__ void store(Smem &sm, int slot, int tid) const {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
@@ -100,139 +94,280 @@ struct Stager {
     }
 };
 
+// One work-group = (batch, KV head g, chunk of positions); wave w serves
+// query head g*G + w (G = NW waves) for every 32-position step of the chunk.
+// Per step and wave the window's key tiles are processed newest first, one
+// at a time: S^T = K Q^T (MFMA), band mask on edge tiles, online softmax
+// whose running max starts at the sink s_h and is only raised when a tile
+// exceeds it by more than 2^8 (so the accumulator is almost never
+// rescaled), P packed to bf16, O^T += V^T P^T (MFMA).  The sink adds
+// exp(s_h - max) to the denominator once at the end.
+//
+// Memory pipeline per wave: Q fragments are double-buffered (the loads for
+// step n+1 are issued when step n starts), the next step's K/V tile is
+// loaded into registers at the start of a step and written into the free
+// ring slot at its end, and output stores are never waited on.  Every
+// global access is a buffer access relative to this work-group's window of
+// the tensor, so rows past the end need no special code.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S,
     int Hq, int Hkv, int W, int ntw, int chunk) {
     constexpr int NT = NW * 64;
-    __shared__ __align__(16) RingSmem<D> sm;
+    constexpr float kSlack = 8.0f;                               // log2 units
+    __shared__ __align__(16) RingSmem<D, NW> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lq = lane & 31, hl = lane >> 5;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int G = Hq / Hkv;
+    const int h = g * NW + wave;
     const int R = ntw + 1;
     const int c0 = blockIdx.x * chunk;
     const int c1 = min(S, c0 + chunk);
     const float c = kLog2e / sqrtf((float)D);
+    // key - query for accumulator register r of a tile starting rel keys
+    // after the step's first query: 16(r>>3) + (r&7) + kbias + rel
+    const int kbias = 8 * hl - lq;
 
-    const size_t row_stride = (size_t)Hkv * D;
-    const bf16 *kb = k + ((size_t)b * S * Hkv + g) * D;
-    const bf16 *vb = v + ((size_t)b * S * Hkv + g) * D;
+    // Buffer windows: q/out rows [c0, c1) of this batch (all heads); k/v rows
+    // [r0, S) of KV head g; lse row of head h.
+    const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
+    const uint32_t rs = (uint32_t)Hkv * D * 2;
+    const int T_first = max(0, c0 / kTile - ntw + 1);
+    const int r0 = kTile * T_first;
+    const rsrc_t qr = make_rsrc(q + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
+    const rsrc_t orr = make_rsrc(out + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
+    const rsrc_t kr = make_rsrc(k + (((size_t)b * S + r0) * Hkv + g) * D, (S - r0) * rs);
+    const rsrc_t vr = make_rsrc(v + (((size_t)b * S + r0) * Hkv + g) * D, (S - r0) * rs);
+    const rsrc_t lr = make_rsrc(lse != nullptr ? lse + ((size_t)b * Hq + h) * S : nullptr,
+                                lse != nullptr ? (uint32_t)S * 4 : 0u);
+    // QK contraction order: lane half hl feeds dims [64hl, 64hl + 64), the
+    // ks-th MFMA step dims 64hl + 8ks .. +8, so each lane reads one whole
+    // 128-byte line of its query row (K fragments use the same order).
+    const uint32_t q_lane = lq * qrow_bytes + D * hl;              // + 16*ks
+    const uint32_t l_lane = hl == 0 ? 4u * lq : kOutOfRange;       // one lane per query
+    const float s2 = sink[h] * kLog2e;
+
+    auto load_q = [&](bf16x8 (&qf)[D / 16], int p0) {
+        const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;    // past the window: zeros
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = buf_load16(qr, q_lane + 16 * ks, so);
+    };
 
     Stager<D, NT> st;
-    {
-        const int T1 = c0 / kTile;
-        for (int T = max(0, T1 - ntw + 1); T <= T1; ++T) {
-            st.load(kb, vb, row_stride, S, T, tid);
-            st.store(sm, T % R, tid);
-        }
+    for (int T = T_first; T <= c0 / kTile; ++T) {
+        st.load(kr, vr, rs, kTile * T - r0, tid);
+        st.store(sm, T % R, tid);
     }
-    __syncthreads();
 
-    for (int p0 = c0; p0 < c1; p0 += kTile) {
+    // S^T of one tile: 32 keys of ring slot `slot` x this wave's 32 queries.
+    auto qk = [&](const bf16x8 (&cur)[D / 16], int slot) {
+        const bf16 *krow = &sm.k[slot][score_row_key(lq)][(D / 2) * hl];
+        f32x16 sc = mfma32(*(const bf16x8 *)krow, cur[0], zero16());
+#pragma unroll
+        for (int ks = 1; ks < D / 16; ++ks)
+            sc = mfma32(*(const bf16x8 *)(krow + 8 * ks), cur[ks], sc);
+        return sc;
+    };
+    // Band mask of a tile starting rel keys after the step's first query.
+    auto band = [&](f32x16 &sc, int rel) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dk = 16 * (r >> 3) + (r & 7) + kbias + rel;
+            sc[r] = (dk <= 0 && dk > -W) ? sc[r] : -INFINITY;
+        }
+    };
+    // One-sided masks for the steady state: the newest tile only needs
+    // key <= query, older tiles only key > query - W (kr <= -kbias and
+    // kr > -W - kbias - rel respectively, kr being a per-register constant).
+    auto causal = [&](f32x16 &sc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sc[r] = (16 * (r >> 3) + (r & 7) <= -kbias) ? sc[r] : -INFINITY;
+    };
+    auto window_edge = [&](f32x16 &sc, int rel) {
+        const int thr = -W - kbias - rel;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sc[r] = (16 * (r >> 3) + (r & 7) > thr) ? sc[r] : -INFINITY;
+    };
+    auto tile_max = [&](const f32x16 &sc) {
+        float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[r], sc[r + 1]));
+        return wave_xor32_max(mx) * c;
+    };
+    // Raise the running max to cover a tile whose max exceeds it by > slack.
+    auto maybe_rescale = [&](float mx, float &m, float &l, f32x16 (&o)[D / 32]) {
+        if (__ballot(mx > m + kSlack) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            m = m_new;
+        }
+    };
+    // P = exp2(S*c - m) packed to bf16 (two K=16 operands); adds to l.
+    auto softmax_tile = [&](f32x16 &sc, float m, float &l, bf16x8 &p0b, bf16x8 &p1b) {
+        const float mu = (m == -INFINITY) ? 0.0f : m;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
+            sc[r] = p;
+            l += p;
+        }
+        p0b = pack8(sc, 0);
+        p1b = pack8(sc, 1);
+    };
+    auto pv = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot) {
+        const int col = slot * kTile + 8 * hl;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col], p0b, o[dt]);
+            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16], p1b, o[dt]);
+        }
+    };
+
+    // One 32-position step with Q fragments `cur`; refills `fill` with the Q
+    // of the next step.
+    auto step = [&](const bf16x8 (&cur)[D / 16], bf16x8 (&fill)[D / 16], int p0) {
         const int T1 = p0 / kTile;
-        const bool has_next = p0 + kTile < c1;
-        if (has_next) st.load(kb, vb, row_stride, S, T1 + 1, tid);
+        lds_barrier();                                           // ring slot T1 staged
+        st.load(kr, vr, rs, kTile * (T1 + 1) - r0, tid);         // next step's tile
+        load_q(fill, p0 + kTile);
 
-        const int pq = p0 + lq;                      // this lane's query position
-        const int pqc = min(pq, S - 1);
-        for (int hh = wave; hh < G; hh += NW) {
-            const int h = g * G + hh;
-            const bf16 *qrow = q + (((size_t)b * S + pqc) * Hq + h) * D + 8 * hl;
-            bf16x8 qf[D / 16];
+        float m = s2;                                            // running max (log2 units)
+        float l = 0.0f;                                          // this lane's share of sum
+        f32x16 o[D / 32];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
-            // S^T tiles (keys x queries), masked to the band [pq - W + 1, pq].
-            f32x16 s[kMaxTiles];
-            float mx = -INFINITY;
+        if (ntw == kMaxTiles && T1 >= kMaxTiles - 1) {
+            // Steady state: the whole window exists.  Software-pipelined so
+            // the matrix and vector units work at once: the QK products of
+            // tile t+1 are issued before the softmax of tile t, and the PV
+            // products of tile t before the mask/max of tile t+1.
+            f32x16 s_cur = qk(cur, T1 % R);
+            causal(s_cur);                                       // W >= 32 here
+            maybe_rescale(tile_max(s_cur), m, l, o);
 #pragma unroll
             for (int t = 0; t < kMaxTiles; ++t) {
-                const int T = T1 - ntw + 1 + t;
-                if (t < ntw && T >= 0) {
-                    const int slot = T % R;
-                    f32x16 acc = zero16();
-                    const bf16 *krow = &sm.k[slot][score_row_key(lq)][8 * hl];
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks)
-                        acc = mfma32(*(const bf16x8 *)(krow + 16 * ks), qf[ks], acc);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kp = kTile * T + score_reg_key(r, lane);
-                        const bool ok = kp <= pq && kp > pq - W;
-                        acc[r] = ok ? acc[r] : -INFINITY;
-                        mx = fmaxf(mx, acc[r]);
-                    }
-                    s[t] = acc;
+                const int T = T1 - t;
+                f32x16 s_next;
+                if (t + 1 < kMaxTiles) s_next = qk(cur, (T - 1) % R);
+                bf16x8 pa, pbb;
+                softmax_tile(s_cur, m, l, pa, pbb);
+                pv(o, pa, pbb, T % R);
+                if (t + 1 < kMaxTiles) {
+                    const int rel = kTile * (T - 1) - p0;
+                    if (rel + W < kTile) window_edge(s_next, rel);
+                    maybe_rescale(tile_max(s_next), m, l, o);
+                    s_cur = s_next;
                 }
             }
-            mx = wave_xor32_max(mx);
+        } else
+#pragma unroll 1
+        for (int t = 0; t < ntw; ++t) {
+            const int T = T1 - t;
+            if (T < 0) break;
+            const int slot = T % R;
+            f32x16 sc = qk(cur, slot);
 
-            // Sink-seeded softmax (log2 domain): max starts at s_h, and the
-            // denominator carries exp(s_h - max) for the virtual sink token.
-            const float s2 = sink[h] * kLog2e;
-            const float m = fmaxf(mx * c, s2);
+            // Band mask: only the newest tile crosses the causal edge and
+            // only tiles reaching back past query - W + 1 cross the window.
+            const int rel = kTile * T - p0;
+            if (t == 0 || rel + W < kTile) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dk = 16 * (r >> 3) + (r & 7) + kbias + rel;
+                    sc[r] = (dk <= 0 && dk > -W) ? sc[r] : -INFINITY;
+                }
+            }
+            float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[r], sc[r + 1]));
+            mx = wave_xor32_max(mx) * c;
+            if (__ballot(mx > m + kSlack) != 0) {                // rare after the first tile
+                const float m_new = fmaxf(m, mx);
+                const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m = m_new;
+            }
             const float mu = (m == -INFINITY) ? 0.0f : m;
-            float l = 0.0f;
 #pragma unroll
-            for (int t = 0; t < kMaxTiles; ++t) {
-                const int T = T1 - ntw + 1 + t;
-                if (t < ntw && T >= 0) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -mu));
-                        s[t][r] = p;
-                        l += p;
-                    }
-                }
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
+                sc[r] = p;
+                l += p;
             }
-            l = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
-
-            // O^T = V^T P^T.
-            f32x16 o[D / 32];
+            const int col = slot * kTile + 8 * hl;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
-#pragma unroll
-            for (int t = 0; t < kMaxTiles; ++t) {
-                const int T = T1 - ntw + 1 + t;
-                if (t < ntw && T >= 0) {
-                    const int slot = T % R;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const bf16x8 pb = pack8(s[t], kk);
-#pragma unroll
-                        for (int dt = 0; dt < D / 32; ++dt) {
-                            const bf16x8 a = *(const bf16x8 *)&sm.vt[32 * dt + lq]
-                                                                    [slot * kTile + 16 * kk + 8 * hl];
-                            o[dt] = mfma32(a, pb, o[dt]);
-                        }
-                    }
-                }
-            }
-
-            if (pq < S) {
-                const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-                bf16 *orow = out + (((size_t)b * S + pq) * Hq + h) * D;
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pb = pack8(sc, kk);
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        bf16x4 w;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dt][4 * j + e] * inv);
-                        *(bf16x4 *)(orow + 32 * dt + 8 * j + 4 * hl) = w;
-                    }
+                    const bf16x8 a = *(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16 * kk];
+                    o[dt] = mfma32(a, pb, o[dt]);
                 }
-                if (lse != nullptr && hl == 0)
-                    lse[((size_t)b * Hq + h) * S + pq] =
-                        l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
             }
         }
 
-        if (has_next) st.store(sm, (T1 + 1) % R, tid);
-        __syncthreads();
+        // The sink joins the denominator once: l = sum_j e^{x_j - m} + e^{s_h - m}.
+        const float mu = (m == -INFINITY) ? 0.0f : m;
+        l = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
+        // Epilogue: out = O / l in bf16 (RNE), transposed through this wave's
+        // LDS staging area 64 dims at a time and stored as full 128-byte row
+        // segments; rows past the window are dropped by the hardware.
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;
+        bf16 (*stg)[64 + 4] = sm.ostage[wave];
+#pragma unroll
+        for (int half = 0; half < D / 64; ++half) {
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[2 * half + dd][4 * jj + e] * inv);
+                    *(bf16x4 *)&stg[lq][32 * dd + 8 * jj + 4 * hl] = w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kTile / 8; ++i) {
+                const int row = 8 * i + (lane >> 3), ch = lane & 7;
+                bf16x8 x;
+                const bf16x4 x0 = *(const bf16x4 *)&stg[row][8 * ch];
+                const bf16x4 x1 = *(const bf16x4 *)&stg[row][8 * ch + 4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = x0[e];
+                    x[4 + e] = x1[e];
+                }
+                buf_store16(x, orr, row * qrow_bytes + 128 * half + 16 * ch, so);
+            }
+        }
+        buf_store_f32(l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY, lr, l_lane,
+                      (uint32_t)p0 * 4);
+
+        if (p0 + kTile < c1) st.store(sm, (T1 + 1) % R, tid);
+    };
+
+    bf16x8 qa[D / 16], qb[D / 16];
+    load_q(qa, c0);
+    for (int p0 = c0; p0 < c1; p0 += 2 * kTile) {
+        step(qa, qb, p0);
+        if (p0 + kTile >= c1) break;
+        step(qb, qa, p0 + kTile);
     }
 }
 
@@ -257,17 +392,21 @@ hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_ring_d(const PrefillArgs &a, hipStream_t stream) {
-    switch (waves_for_group(a.Hq / a.Hkv)) {
-    case 8: return launch_ring<D, 8>(a, stream);
-    case 4: return launch_ring<D, 4>(a, stream);
+    switch (a.Hq / a.Hkv) {          // one wave per query head of the group
+    case 1: return launch_ring<D, 1>(a, stream);
     case 2: return launch_ring<D, 2>(a, stream);
-    default: return launch_ring<D, 1>(a, stream);
+    case 4: return launch_ring<D, 4>(a, stream);
+    case 8: return launch_ring<D, 8>(a, stream);
+    default: return hipErrorNotSupported;
     }
 }
 
 }  // namespace
 
-bool prefill_ring_supported(int window) { return window >= 1 && window <= 129; }
+bool prefill_ring_supported(int window, int G) {
+    const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+    return window >= 1 && window <= 129 && g_ok;
+}
 
 hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream) {
     return a.D == 64 ? launch_ring_d<64>(a, stream) : launch_ring_d<128>(a, stream);
