@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-    "-fvisibility=hidden", "-ffp-contract=fast",
+    "-fvisibility=hidden", "-ffp-contract=fast", "-fno-strict-aliasing",
     # packed fp32 arithmetic stays off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,

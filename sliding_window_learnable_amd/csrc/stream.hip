@@ -81,15 +81,19 @@ struct TileLoader {
             const int item = tid + i * NT;
             if (item < 8 * CH) {
                 const int kq = item & 7, ch = item >> 3;
+                u32x2 w[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    bf16x4 w;
-                    w[0] = vreg[i][0][e];
-                    w[1] = vreg[i][1][e];
-                    w[2] = vreg[i][2][e];
-                    w[3] = vreg[i][3][e];
-                    *(bf16x4 *)&sm.vt[slot][8 * ch + e][4 * kq] = w;
+                    bf16x4 x;
+                    x[0] = vreg[i][0][e];
+                    x[1] = vreg[i][1][e];
+                    x[2] = vreg[i][2][e];
+                    x[3] = vreg[i][3][e];
+                    w[e] = __builtin_bit_cast(u32x2, x);
+                    *(u32x2 *)&sm.vt[slot][8 * ch + e][4 * kq] = w[e];
                 }
+                // Issued while this step's PV products may still be running.
+                lds_settle(w);
             }
         }
     }

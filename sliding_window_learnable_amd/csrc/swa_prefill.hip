@@ -36,7 +36,7 @@ struct RingSmem {
     bf16 vt[D][kRingKeys + 8];
     // Per-wave output staging: 32 queries x 64 dims (half of D = 128 at a
     // time), so that global stores are whole 128-byte row segments.
-    bf16 ostage[NW][kTile][64 + 4];
+    bf16 ostage[NW][kTile][64 + 8];
 };
 
 // Stages one 32-key tile: K rows as 16-byte chunks into sm.k[slot], V as
@@ -233,6 +233,15 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         }
     };
 
+    auto pv_first = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot) {
+        const int col = slot * kTile + 8 * hl;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col], p0b, zero16());
+            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16], p1b, o[dt]);
+        }
+    };
+
     // One 32-position step with Q fragments `cur`; refills `fill` with the Q
     // of the next step.
     auto step = [&](const bf16x8 (&cur)[D / 16], bf16x8 (&fill)[D / 16], int p0) {
@@ -244,80 +253,37 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         float m = s2;                                            // running max (log2 units)
         float l = 0.0f;                                          // this lane's share of sum
         f32x16 o[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
-        if (ntw == kMaxTiles && T1 >= kMaxTiles - 1) {
-            // Steady state: the whole window exists.  Software-pipelined so
-            // the matrix and vector units work at once: the QK products of
-            // tile t+1 are issued before the softmax of tile t, and the PV
-            // products of tile t before the mask/max of tile t+1.
-            f32x16 s_cur = qk(cur, T1 % R);
-            causal(s_cur);                                       // W >= 32 here
-            maybe_rescale(tile_max(s_cur), m, l, o);
+        // The window is processed newest tile first (98 <= W <= 129: five
+        // tiles).  Software-pipelined so the matrix and vector units work at
+        // once: the QK products of tile t+1 are issued before the softmax of
+        // tile t, the PV products of tile t before the mask/max of tile t+1.
+        // Tile 0 needs the causal mask, tile 4 (and tile 3 when W < 128) the
+        // window edge; in the first four steps of a sequence, tiles before
+        // position 0 read any resident slot and are masked out entirely.
+        f32x16 s_cur = qk(cur, T1 % R);
+        causal(s_cur);
+        m = fmaxf(m, tile_max(s_cur));                           // nothing accumulated yet
 #pragma unroll
-            for (int t = 0; t < kMaxTiles; ++t) {
-                const int T = T1 - t;
-                f32x16 s_next;
-                if (t + 1 < kMaxTiles) s_next = qk(cur, (T - 1) % R);
-                bf16x8 pa, pbb;
-                softmax_tile(s_cur, m, l, pa, pbb);
-                pv(o, pa, pbb, T % R);
-                if (t + 1 < kMaxTiles) {
-                    const int rel = kTile * (T - 1) - p0;
-                    if (rel + W < kTile) window_edge(s_next, rel);
-                    maybe_rescale(tile_max(s_next), m, l, o);
-                    s_cur = s_next;
-                }
-            }
-        } else
-#pragma unroll 1
-        for (int t = 0; t < ntw; ++t) {
+        for (int t = 0; t < kMaxTiles; ++t) {
             const int T = T1 - t;
-            if (T < 0) break;
-            const int slot = T % R;
-            f32x16 sc = qk(cur, slot);
-
-            // Band mask: only the newest tile crosses the causal edge and
-            // only tiles reaching back past query - W + 1 cross the window.
-            const int rel = kTile * T - p0;
-            if (t == 0 || rel + W < kTile) {
+            f32x16 s_next;
+            if (t + 1 < kMaxTiles) s_next = qk(cur, (T >= 1 ? T - 1 : T1) % R);
+            bf16x8 pa, pbb;
+            softmax_tile(s_cur, m, l, pa, pbb);
+            if (t == 0)
+                pv_first(o, pa, pbb, T1 % R);
+            else
+                pv(o, pa, pbb, (T >= 0 ? T : T1) % R);
+            if (t + 1 < kMaxTiles) {
+                if (T - 1 < 0) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dk = 16 * (r >> 3) + (r & 7) + kbias + rel;
-                    sc[r] = (dk <= 0 && dk > -W) ? sc[r] : -INFINITY;
+                    for (int r = 0; r < 16; ++r) s_next[r] = -INFINITY;
+                } else if (t + 1 == kMaxTiles - 1 || (t + 1 == kMaxTiles - 2 && W < 4 * kTile)) {
+                    window_edge(s_next, -kTile * (t + 1));
                 }
-            }
-            float mx = fmaxf(sc[0], sc[1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[r], sc[r + 1]));
-            mx = wave_xor32_max(mx) * c;
-            if (__ballot(mx > m + kSlack) != 0) {                // rare after the first tile
-                const float m_new = fmaxf(m, mx);
-                const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
-                l *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-                m = m_new;
-            }
-            const float mu = (m == -INFINITY) ? 0.0f : m;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
-                sc[r] = p;
-                l += p;
-            }
-            const int col = slot * kTile + 8 * hl;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pb = pack8(sc, kk);
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16 * kk];
-                    o[dt] = mfma32(a, pb, o[dt]);
-                }
+                maybe_rescale(tile_max(s_next), m, l, o);
+                s_cur = s_next;
             }
         }
 
@@ -326,35 +292,35 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         l = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
         // Epilogue: out = O / l in bf16 (RNE), transposed through this wave's
         // LDS staging area 64 dims at a time and stored as full 128-byte row
-        // segments; rows past the window are dropped by the hardware.
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        // segments; rows past the window are dropped by the hardware.  The
+        // staging writes are issued while the last PV products may still be
+        // running, so their data registers are held until they complete.
+        const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
         const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;
-        bf16 (*stg)[64 + 4] = sm.ostage[wave];
+        bf16 (*stg)[64 + 8] = sm.ostage[wave];
 #pragma unroll
         for (int half = 0; half < D / 64; ++half) {
+            u32x2 w[8];
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    bf16x4 w;
+                    bf16x4 x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[2 * half + dd][4 * jj + e] * inv);
-                    *(bf16x4 *)&stg[lq][32 * dd + 8 * jj + 4 * hl] = w;
+                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[2 * half + dd][4 * jj + e] * inv);
+                    w[4 * dd + jj] = __builtin_bit_cast(u32x2, x);
+                    *(u32x2 *)&stg[lq][32 * dd + 8 * jj + 4 * hl] = w[4 * dd + jj];
                 }
             }
+            lds_settle(w);
+            const int ch = lane & 7;
+            bf16x8 x[kTile / 8];
 #pragma unroll
-            for (int i = 0; i < kTile / 8; ++i) {
-                const int row = 8 * i + (lane >> 3), ch = lane & 7;
-                bf16x8 x;
-                const bf16x4 x0 = *(const bf16x4 *)&stg[row][8 * ch];
-                const bf16x4 x1 = *(const bf16x4 *)&stg[row][8 * ch + 4];
+            for (int i = 0; i < kTile / 8; ++i) x[i] = *(const bf16x8 *)&stg[8 * i + (lane >> 3)][8 * ch];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = x0[e];
-                    x[4 + e] = x1[e];
-                }
-                buf_store16(x, orr, row * qrow_bytes + 128 * half + 16 * ch, so);
-            }
+            for (int i = 0; i < kTile / 8; ++i)
+                buf_store16(x[i], orr, (8 * i + (lane >> 3)) * qrow_bytes + 128 * half + 16 * ch, so);
+            asm volatile("" ::: "memory");             // next half's writes after these reads
         }
         buf_store_f32(l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY, lr, l_lane,
                       (uint32_t)p0 * 4);
@@ -405,7 +371,7 @@ hipError_t launch_ring_d(const PrefillArgs &a, hipStream_t stream) {
 
 bool prefill_ring_supported(int window, int G) {
     const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
-    return window >= 1 && window <= 129 && g_ok;
+    return window >= 98 && window <= 129 && g_ok;         // exactly five 32-key tiles
 }
 
 hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream) {

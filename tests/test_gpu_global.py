@@ -98,3 +98,18 @@ def test_global_64k_real_token_mass_identity(gpu):
     expect = mass.permute(0, 2, 1)[..., None].expand(B, S, Hq, D)
     err = (out.double() - expect).abs()
     assert bool((err <= 2e-2 + 1e-2 * expect.abs()).all()), float(err.max())
+
+
+def test_stream_repeat_runs_bit_identical(gpu):
+    """Repeated runs of the streaming kernel (global causal layer, and a wide
+    window) on the same inputs are bit-identical and finite."""
+    q, k, v, sink = inputs.attention_inputs(96, 0, 1, 4096, 4096, 64, 8, 128, torch.bfloat16, "cuda")
+    o1, l1 = swa.global_sink_attn(q, k, v, sink)
+    w1, wl1 = swa.swa_sink_prefill(q, k, v, sink, 1000)
+    assert bool(torch.isfinite(o1).all()) and bool(torch.isfinite(w1).all())
+    for _ in range(6):
+        o2, l2 = swa.global_sink_attn(q, k, v, sink)
+        w2, wl2 = swa.swa_sink_prefill(q, k, v, sink, 1000)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.equal(w1, w2) and torch.equal(wl1, wl2)
