@@ -88,13 +88,17 @@ __device__ __forceinline__ void lds_barrier() {
 // in flight, bank-conflicted lanes) the LDS unit can read them later than
 // the next instructions that reuse them.  Naming them as operands keeps
 // them intact until the writes are complete.
-template <class V>
-__device__ __forceinline__ void lds_settle(const V (&w)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 :
-                 : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]),
-                   "v"(w[7])
-                 : "memory");
+template <class V, int N>
+__device__ __forceinline__ void lds_settle(const V (&w)[N]) {
+    static_assert(N == 4 || N == 8, "lds_settle holds 4 or 8 registers");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     :
+                     : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]),
+                       "v"(w[6]), "v"(w[7])
+                     : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]) : "memory");
 }
 
 // ---------------------------------------------------------------------------
