@@ -90,15 +90,19 @@ __device__ __forceinline__ void lds_barrier() {
 // them intact until the writes are complete.
 template <class V, int N>
 __device__ __forceinline__ void lds_settle(const V (&w)[N]) {
-    static_assert(N == 4 || N == 8, "lds_settle holds 4 or 8 registers");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "lds_settle holds 1, 2, 4 or 8 registers");
     if constexpr (N == 8)
         asm volatile("s_waitcnt lgkmcnt(0)"
                      :
                      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]),
                        "v"(w[6]), "v"(w[7])
                      : "memory");
-    else
+    else if constexpr (N == 4)
         asm volatile("s_waitcnt lgkmcnt(0)" : : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]) : "memory");
+    else if constexpr (N == 2)
+        asm volatile("s_waitcnt lgkmcnt(0)" : : "v"(w[0]), "v"(w[1]) : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : : "v"(w[0]) : "memory");
 }
 
 // ---------------------------------------------------------------------------

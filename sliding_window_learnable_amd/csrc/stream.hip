@@ -13,10 +13,16 @@
 //   some column grows by more than 2^8, so exp2 arguments stay <= 8),
 //   O^T += V^T P^T (bf16 MFMA).
 // At the end the sink's exp(s_h - max) joins the denominator exactly once.
-// Tiles are double-buffered: tile T+1 is fetched into registers while tile
-// T is computed.  Work-groups are issued longest-first (the last query
-// blocks have the most keys) with the (batch, KV head) index fastest, so
-// the blocks of one KV head share an XCD and its L2.
+//
+// Pipeline: key tiles live in an LDS ring of three slots.  At the top of
+// iteration t the slots hold tiles t and t+1 and tile t+2 is in flight in
+// registers; a wave issues the S^T products of tile t+1 before the softmax
+// of tile t (so the matrix unit and the vector unit work at once), then the
+// PV products of tile t, then the max of tile t+1.  At the end of the
+// iteration tile t+2 is written to the slot freed by tile t-1 and tile t+3
+// is requested.  One barrier per tile.  Work-groups are issued longest-first
+// (the last query blocks have the most keys) with the (batch, KV head)
+// index fastest, so the blocks of one KV head share an XCD and its L2.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -24,57 +30,59 @@ namespace swa {
 namespace {
 
 constexpr int kTile = 32;
+constexpr int kSlots = 3;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 
 template <int D>
 struct StreamSmem {
-    bf16 k[2][kTile][D + 8];
-    bf16 vt[2][D][kTile + 8];
+    bf16 k[kSlots][kTile][D + 8];        // row stride 2D+16 bytes: conflict-free fragment reads
+    bf16 vt[kSlots][D][kTile + 8];       // V^T, row stride 80 bytes: conflict-free fragment reads
 };
 
+// Loads one 32-key tile into registers (K as 16-byte row pieces, V as
+// 4-key x 8-dim quads) and writes it to a ring slot, V transposed.  The
+// buffer descriptor covers only the tile's rows that exist, so rows past
+// the end of the keys read as zeros.
 template <int D, int NT>
 struct TileLoader {
-    static constexpr int CH = D / 8;
+    static constexpr int CH = D / 8;                       // 16-byte pieces per row
     static constexpr int KPT = (kTile * CH + NT - 1) / NT;
     static constexpr int VPT = (8 * CH + NT - 1) / NT;
     bf16x8 kreg[KPT];
     bf16x8 vreg[VPT][4];
 
-    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, size_t row_stride,
-                                         int S_kv, int T, int tid) {
-        bf16x8 z;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, size_t row_elems,
+                                         uint32_t rs, int S_kv, int T, int tid) {
+        const int rows = min(kTile, S_kv - kTile * T);
+        const uint32_t bytes = rows > 0 ? (uint32_t)rows * rs : 0u;
+        const rsrc_t kr = make_rsrc(kb + (size_t)kTile * T * row_elems, bytes);
+        const rsrc_t vr = make_rsrc(vb + (size_t)kTile * T * row_elems, bytes);
+        // Item counts are multiples of 64, so the guards are wave-uniform.
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int item = tid + i * NT;
-            kreg[i] = z;
-            if (item < kTile * CH) {
-                const int pos = kTile * T + item / CH, ch = item % CH;
-                if (pos < S_kv) kreg[i] = *(const bf16x8 *)(kb + (size_t)pos * row_stride + 8 * ch);
-            }
+            if (item < kTile * CH) kreg[i] = buf_load16(kr, (item / CH) * rs + 16 * (item % CH), 0);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int item = tid + i * NT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vreg[i][j] = z;
             if (item < 8 * CH) {
-                const int kq = item & 7, ch = item >> 3;
+                const uint32_t vo = 4 * (item & 7) * rs + 16 * (item >> 3);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int pos = kTile * T + 4 * kq + j;
-                    if (pos < S_kv) vreg[i][j] = *(const bf16x8 *)(vb + (size_t)pos * row_stride + 8 * ch);
-                }
+                for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, vo + j * rs, 0);
             }
         }
     }
 
     __device__ __forceinline__ void store(StreamSmem<D> &sm, int slot, int tid) const {
+        if (tid < kTile * CH) {                            // wave-uniform
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < kTile * CH) *(bf16x8 *)&sm.k[slot][item / CH][8 * (item % CH)] = kreg[i];
+            for (int i = 0; i < KPT; ++i) {
+                const int item = tid + i * NT;
+                if (item < kTile * CH) *(bf16x8 *)&sm.k[slot][item / CH][8 * (item % CH)] = kreg[i];
+            }
+            // The data registers take the next tile's loads right after.
+            lds_settle(kreg);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -92,7 +100,7 @@ struct TileLoader {
                     w[e] = __builtin_bit_cast(u32x2, x);
                     *(u32x2 *)&sm.vt[slot][8 * ch + e][4 * kq] = w[e];
                 }
-                // Issued while this step's PV products may still be running.
+                // Written while this wave's PV products may still be running.
                 lds_settle(w);
             }
         }
@@ -117,27 +125,42 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const float c = kLog2e / sqrtf((float)D);
 
     const int i0 = qb * kTile;                         // first query row of the block
-    const long off = (long)S_kv - S_q;                 // row i sits at position off + i
-    const long p_first = off + i0;
-    const long p_last = off + min(S_q - 1, i0 + kTile - 1);
-    const int T_lo = (int)max(0L, (p_first - W + 1) >= 0 ? (p_first - W + 1) / kTile : 0L);
-    const int T_hi = (int)(p_last / kTile);
+    const int off = S_kv - S_q;                        // row i sits at position off + i
+    const int p_first = off + i0;
+    const int p_last = off + min(S_q - 1, i0 + kTile - 1);
+    const int T_lo = max(0, p_first - W + 1) / kTile;
+    const int T_hi = p_last / kTile;
+    const int n_tiles = T_hi - T_lo + 1;
 
-    const size_t row_stride = (size_t)Hkv * D;
+    const size_t row_elems = (size_t)Hkv * D;
+    const uint32_t rs = (uint32_t)row_elems * 2;
     const bf16 *kb = k + ((size_t)b * S_kv * Hkv + g) * D;
     const bf16 *vb = v + ((size_t)b * S_kv * Hkv + g) * D;
 
     const int i = i0 + lq;                             // this lane's query row
     const bool row_ok = i < S_q;
-    const long pq = off + min(i, S_q - 1);
+    const int pq = off + min(i, S_q - 1);
+    // key - query for accumulator register r of tile T:
+    //   32T + 16(r>>3) + (r&7) + kbias
+    const int kbias = 8 * hl - pq;
 
     TileLoader<D, NT> ld;
-    ld.load(kb, vb, row_stride, S_kv, T_lo, tid);
-    ld.store(sm, 0, tid);
-    lds_barrier();
+    auto tile_keys_masked = [&](int T) {               // wave-uniform
+        return kTile * T + kTile - 1 > p_first || kTile * T <= p_last - W;
+    };
 
     for (int hh = wave; hh < G; hh += NW) {
         const int h = g * G + hh;
+        if (hh != wave) lds_barrier();                 // previous head's reads are done
+        // Prologue: tiles 0 and 1 into slots 0 and 1, tile 2 in flight.
+        ld.load(kb, vb, row_elems, rs, S_kv, T_lo, tid);
+        ld.store(sm, 0, tid);
+        if (n_tiles > 1) {
+            ld.load(kb, vb, row_elems, rs, S_kv, T_lo + 1, tid);
+            ld.store(sm, 1, tid);
+        }
+        if (n_tiles > 2) ld.load(kb, vb, row_elems, rs, S_kv, T_lo + 2, tid);
+
         bf16x8 qf[D / 16];
         {
             const bf16 *qrow = q + (((size_t)b * S_q + min(i, S_q - 1)) * Hq + h) * D + 8 * hl;
@@ -151,39 +174,31 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
-        for (int T = T_lo; T <= T_hi; ++T) {
-            const int slot = (T - T_lo) & 1;
-            const bool prefetch = T < T_hi;
-            if (prefetch) ld.load(kb, vb, row_stride, S_kv, T + 1, tid);
-
-            f32x16 s = zero16();
+        auto qk = [&](int slot) {
             const bf16 *krow = &sm.k[slot][score_row_key(lq)][8 * hl];
+            f32x16 sc = mfma32(*(const bf16x8 *)krow, qf[0], zero16());
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) s = mfma32(*(const bf16x8 *)(krow + 16 * ks), qf[ks], s);
-
-            const long k0 = (long)kTile * T;
-            const bool interior = k0 + kTile - 1 <= p_first && k0 >= p_last - W + 1;
-            float mx = -INFINITY;
-            if (interior) {
+            for (int ks = 1; ks < D / 16; ++ks)
+                sc = mfma32(*(const bf16x8 *)(krow + 16 * ks), qf[ks], sc);
+            return sc;
+        };
+        auto mask = [&](f32x16 &sc, int T) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const long kp = k0 + score_reg_key(r, lane);
-                    const bool ok = kp <= pq && kp > pq - W;
-                    s[r] = ok ? s[r] : -INFINITY;
-                    mx = fmaxf(mx, s[r]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int dk = kTile * T + 16 * (r >> 3) + (r & 7) + kbias;
+                sc[r] = (dk <= 0 && dk > -W) ? sc[r] : -INFINITY;
             }
-            mx = wave_xor32_max(mx) * c;
-
-            // Lazy rescale: only when some column's max grew by > 2^slack.
+        };
+        auto tile_max = [&](const f32x16 &sc) {
+            float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[r], sc[r + 1]));
+            return wave_xor32_max(mx) * c;
+        };
+        auto maybe_rescale = [&](float mx) {
             if (__ballot(mx > m + kRescaleSlack) != 0) {
                 const float m_new = fmaxf(m, mx);
-                const float alpha = (m_new == -INFINITY || m == -INFINITY)
-                                        ? (m_new == -INFINITY ? 1.0f : 0.0f)
-                                        : __builtin_amdgcn_exp2f(m - m_new);
+                const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - m_new);
                 l *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
@@ -191,31 +206,54 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
                     for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
                 m = m_new;
             }
+        };
+
+        lds_barrier();                                 // slots 0 and 1 staged
+        f32x16 s_cur = qk(0);
+        if (tile_keys_masked(T_lo)) mask(s_cur, T_lo);
+        // Nothing accumulated yet: the first tile only raises the max.
+        m = fmaxf(m, tile_max(s_cur));
+
+        for (int t = 0; t < n_tiles; ++t) {
+            const int T = T_lo + t;
+            const bool more = t + 1 < n_tiles;
+            if (t > 0) lds_barrier();                  // tile t+1 staged, tile t-1 released
+            f32x16 s_next;
+            if (more) s_next = qk((t + 1) % kSlots);
+
             const float mu = (m == -INFINITY) ? 0.0f : m;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mu));
-                s[r] = p;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
+                s_cur[r] = p;
                 l += p;
             }
+            const bf16x8 pa = pack8(s_cur, 0), pb = pack8(s_cur, 1);
+            const int slot = t % kSlots;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pb = pack8(s, kk);
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][16 * kk + 8 * hl];
-                    o[dt] = mfma32(a, pb, o[dt]);
-                }
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const bf16x8 a0 = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][8 * hl];
+                const bf16x8 a1 = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][16 + 8 * hl];
+                o[dt] = mfma32(a0, pa, o[dt]);
+                o[dt] = mfma32(a1, pb, o[dt]);
             }
-            if (prefetch) ld.store(sm, slot ^ 1, tid);
-            lds_barrier();
+
+            if (more) {
+                if (tile_keys_masked(T + 1)) mask(s_next, T + 1);
+                maybe_rescale(tile_max(s_next));
+                s_cur = s_next;
+            }
+            if (t + 2 < n_tiles) {
+                ld.store(sm, (t + 2) % kSlots, tid);
+                if (t + 3 < n_tiles) ld.load(kb, vb, row_elems, rs, S_kv, T + 3, tid);
+            }
         }
 
         // Sink joins the denominator once: l_total = sum_j e^{x_j - m} + e^{s_h - m}.
         const float mu = (m == -INFINITY) ? 0.0f : m;
         const float lt = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
         if (row_ok) {
-            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            const float inv = lt > 0.0f ? __builtin_amdgcn_rcpf(lt) : 0.0f;
             bf16 *orow = out + (((size_t)b * S_q + i) * Hq + h) * D;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
@@ -230,13 +268,6 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             if (lse != nullptr && hl == 0)
                 lse[((size_t)b * Hq + h) * S_q + i] =
                     lt > 0.0f ? (mu + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-        }
-        if (hh + NW < G) {
-            // next head of this wave: restage the first tile
-            lds_barrier();
-            ld.load(kb, vb, row_stride, S_kv, T_lo, tid);
-            ld.store(sm, 0, tid);
-            lds_barrier();
         }
     }
 }
