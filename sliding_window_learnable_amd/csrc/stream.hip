@@ -32,6 +32,7 @@ namespace {
 constexpr int kTile = 32;
 constexpr int kSlots = 3;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
+constexpr float kBig = 256.0f;           // 2^kRescaleSlack
 
 template <int D>
 struct StreamSmem {
@@ -176,10 +177,12 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 
         auto qk = [&](int slot) {
             const bf16 *krow = &sm.k[slot][score_row_key(lq)][8 * hl];
-            f32x16 sc = mfma32(*(const bf16x8 *)krow, qf[0], zero16());
+            bf16x8 a[D / 16];
 #pragma unroll
-            for (int ks = 1; ks < D / 16; ++ks)
-                sc = mfma32(*(const bf16x8 *)(krow + 16 * ks), qf[ks], sc);
+            for (int ks = 0; ks < D / 16; ++ks) a[ks] = *(const bf16x8 *)(krow + 16 * ks);
+            f32x16 sc = mfma32(a[0], qf[0], zero16());
+#pragma unroll
+            for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], qf[ks], sc);
             return sc;
         };
         auto mask = [&](f32x16 &sc, int T) {
@@ -218,29 +221,47 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             const int T = T_lo + t;
             const bool more = t + 1 < n_tiles;
             if (t > 0) lds_barrier();                  // tile t+1 staged, tile t-1 released
-            f32x16 s_next;
-            if (more) s_next = qk((t + 1) % kSlots);
+            // Past the last tile the product reads a stale slot and is discarded.
+            f32x16 s_next = qk((t + 1) % kSlots);
 
-            const float mu = (m == -INFINITY) ? 0.0f : m;
+            // P = exp2(S c - m).  The max is taken on P (canonical exp2
+            // outputs: max3 without canonicalisation); if some P exceeds
+            // 2^slack the running max fell behind: raise it to the tile's
+            // exact max, rescale, recompute.  A column whose max is still
+            // -inf uses an offset that sends any finite score to +inf.
+            f32x16 p;
+            {
+                const float mu = (m == -INFINITY) ? -3.0e38f : m;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
-                s_cur[r] = p;
-                l += p;
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
             }
-            const bf16x8 pa = pack8(s_cur, 0), pb = pack8(s_cur, 1);
+            float pmax = fmaxf(p[0], p[1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) pmax = fmaxf(pmax, fmaxf(p[r], p[r + 1]));
+            if (__ballot(pmax > kBig) != 0) {
+                maybe_rescale(tile_max(s_cur));
+                const float mu = (m == -INFINITY) ? -3.0e38f : m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) l += p[r];
+            const bf16x8 pa = pack8(p, 0), pb = pack8(p, 1);
             const int slot = t % kSlots;
+            bf16x8 va[D / 32][2];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x8 a0 = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][8 * hl];
-                const bf16x8 a1 = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][16 + 8 * hl];
-                o[dt] = mfma32(a0, pa, o[dt]);
-                o[dt] = mfma32(a1, pb, o[dt]);
+                va[dt][0] = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][8 * hl];
+                va[dt][1] = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][16 + 8 * hl];
+            }
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                o[dt] = mfma32(va[dt][0], pa, o[dt]);
+                o[dt] = mfma32(va[dt][1], pb, o[dt]);
             }
 
             if (more) {
                 if (tile_keys_masked(T + 1)) mask(s_next, T + 1);
-                maybe_rescale(tile_max(s_next));
                 s_cur = s_next;
             }
             if (t + 2 < n_tiles) {

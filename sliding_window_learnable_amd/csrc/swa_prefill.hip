@@ -116,6 +116,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     int Hq, int Hkv, int W, int ntw, int chunk) {
     constexpr int NT = NW * 64;
     constexpr float kSlack = 8.0f;                               // log2 units
+    constexpr float kBig = 256.0f;                               // 2^kSlack
     __shared__ __align__(16) RingSmem<D, NW> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -213,16 +214,31 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         }
     };
     // P = exp2(S*c - m) packed to bf16 (two K=16 operands); adds to l.
-    auto softmax_tile = [&](f32x16 &sc, float m, float &l, bf16x8 &p0b, bf16x8 &p1b) {
-        const float mu = (m == -INFINITY) ? 0.0f : m;
+    // The max is taken on P (canonical exp2 outputs); if some P exceeds
+    // 2^slack the running max fell behind: raise it to the tile's exact
+    // max, rescale, recompute.  A column whose max is still -inf uses an
+    // offset that sends any finite score to +inf.
+    auto softmax_tile = [&](f32x16 &sc, float &m, float &l, f32x16 (&o)[D / 32], bf16x8 &p0b,
+                            bf16x8 &p1b) {
+        f32x16 p;
+        {
+            const float mu = (m == -INFINITY) ? -3.0e38f : m;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
-            sc[r] = p;
-            l += p;
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
         }
-        p0b = pack8(sc, 0);
-        p1b = pack8(sc, 1);
+        float pm = fmaxf(p[0], p[1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) pm = fmaxf(pm, fmaxf(p[r], p[r + 1]));
+        if (__ballot(pm > kBig) != 0) {
+            maybe_rescale(tile_max(sc), m, l, o);
+            const float mu = (m == -INFINITY) ? -3.0e38f : m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) l += p[r];
+        p0b = pack8(p, 0);
+        p1b = pack8(p, 1);
     };
     auto pv = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot) {
         const int col = slot * kTile + 8 * hl;
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             f32x16 s_next;
             if (t + 1 < kMaxTiles) s_next = qk(cur, (T >= 1 ? T - 1 : T1) % R);
             bf16x8 pa, pbb;
-            softmax_tile(s_cur, m, l, pa, pbb);
+            softmax_tile(s_cur, m, l, o, pa, pbb);
             if (t == 0)
                 pv_first(o, pa, pbb, T1 % R);
             else
@@ -282,7 +298,6 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
                 } else if (t + 1 == kMaxTiles - 1 || (t + 1 == kMaxTiles - 2 && W < 4 * kTile)) {
                     window_edge(s_next, -kTile * (t + 1));
                 }
-                maybe_rescale(tile_max(s_next), m, l, o);
                 s_cur = s_next;
             }
         }
