@@ -129,6 +129,16 @@ __device__ __forceinline__ void buf_store8(bf16x4 v, rsrc_t r, uint32_t voff, ui
 __device__ __forceinline__ void buf_store16(bf16x8 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
 }
+// Streaming load (cache policy "nt") for data read exactly once, in whole
+// cache lines per instruction.
+__device__ __forceinline__ bf16x8 buf_load16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+// Streaming store (cache policy "nt"): output written once and not read
+// back by this kernel.  Whole 128-byte segments only.
+__device__ __forceinline__ void buf_store16_nt(bf16x8 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 2);
+}
 __device__ __forceinline__ void buf_store_f32(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
 }

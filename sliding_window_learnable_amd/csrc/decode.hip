@@ -108,7 +108,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
         for (int ks = 0; ks < KF; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 8 * ks);
     }
     // K is loaded whole rows at a time (16 lanes per 256-byte row, so every
-    // load instruction covers full cache lines) and turned into MFMA
+    // load instruction covers full cache lines; K and V are read once, so the
+    // loads are non-temporal) and turned into MFMA
     // fragments through the wave's LDS tile.  Load u, lane i: 16-byte piece
     // e = 64u + i of the chunk, row e / (D/8), column piece e % (D/8).
     bf16x8 kf[KF];                                   // K rows (16-byte pieces) of the current chunk
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
 #pragma unroll
         for (int u = 0; u < KF; ++u) {
             const int e = 64 * u + lane;
-            kf[u] = buf_load16(kr, (e / (D / 8)) * rs + 16 * (e % (D / 8)), (uint32_t)k0 * rs);
+            kf[u] = buf_load16_nt(kr, (e / (D / 8)) * rs + 16 * (e % (D / 8)), (uint32_t)k0 * rs);
         }
     };
     auto load_v = [&](int k0) {
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
             const int it = lane + 64 * i, kq = it & 7, ch = it >> 3;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                vq[i][j] = buf_load16(vr, (4 * kq + j) * rs + 16 * ch, (uint32_t)k0 * rs);
+                vq[i][j] = buf_load16_nt(vr, (4 * kq + j) * rs + 16 * ch, (uint32_t)k0 * rs);
         }
     };
 

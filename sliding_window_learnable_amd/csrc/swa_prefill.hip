@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             for (int i = 0; i < kTile / 8; ++i) x[i] = *(const bf16x8 *)&stg[8 * i + (lane >> 3)][8 * ch];
 #pragma unroll
             for (int i = 0; i < kTile / 8; ++i)
-                buf_store16(x[i], orr, (8 * i + (lane >> 3)) * qrow_bytes + 128 * half + 16 * ch, so);
+                buf_store16_nt(x[i], orr, (8 * i + (lane >> 3)) * qrow_bytes + 128 * half + 16 * ch, so);
             asm volatile("" ::: "memory");             // next half's writes after these reads
         }
         buf_store_f32(l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY, lr, l_lane,
