@@ -200,6 +200,7 @@ def bench_hybrid(args, swa, acc, torch):
     f_swa = acc.prefill_flops(B, S, Hq, D, W)
     f_ga = acc.global_flops(B, S, S, Hq, D)
     compute_red, kv_red = acc.hybrid_ratios(S, W, 5)
+    compute_red7, kv_red7 = acc.hybrid_ratios(S, W, 7)
     del layers
     torch.cuda.empty_cache()
     return {
@@ -215,6 +216,13 @@ def bench_hybrid(args, swa, acc, torch):
         "attention_compute_reduction_vs_6_global": compute_red,
         "kv_cache_reduction_vs_6_global": kv_red,
         "measured_time_reduction_vs_6_global": 6 * ms_ga / (ms_swa5 + ms_ga),
+        # 7:1 schedule (Pro): the same two layer types, 7 SWA layers per global one
+        "schedule_7to1": {
+            "stack_ms": 7 * ms_swa5 / 5 + ms_ga,
+            "attention_compute_reduction_vs_8_global": compute_red7,
+            "kv_cache_reduction_vs_8_global": kv_red7,
+            "measured_time_reduction_vs_8_global": 8 * ms_ga / (7 * ms_swa5 / 5 + ms_ga),
+        },
     }
 
 

@@ -66,8 +66,10 @@ enum swa_status {
     SWA_OK = 0,
     SWA_ERR_NULL = -1,        /* a required pointer is NULL                        */
     SWA_ERR_SHAPE = -2,       /* negative size, Hq/Hkv/D/window < 1, Hq % Hkv != 0,
-                                 T_q > window, S_q > S_kv, B or Hq > 65535         */
-    SWA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, unknown dtype, misaligned pointer */
+                                 T_q > window, S_q > S_kv, B or Hq > 65535, or more
+                                 work units (B*Hq*rows/32, B*Hq*T_q) than 2^31-1  */
+    SWA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, unknown dtype, misaligned pointer,
+                                 or window*D*2 > 2^31-1 bytes for one decode ring  */
     SWA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
     SWA_ERR_HIP = -5          /* the HIP runtime reported an error at launch       */
 };

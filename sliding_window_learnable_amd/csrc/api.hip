@@ -26,6 +26,10 @@ int common_checks(int B, int Hq, int Hkv, int D, int dtype) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 
+// Work-groups / work items of one launch must fit a 31-bit grid dimension.
+constexpr long kMaxGridX = 0x7fffffffL;
+bool grid_fits(long units) { return units >= 0 && units <= kMaxGridX; }
+
 }  // namespace
 
 extern "C" {
@@ -41,6 +45,7 @@ int swa_sink_prefill(const void *q, const void *k, const void *v, const float *s
         !aligned(sink, 4) || !aligned(lse, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hkv * ((S + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
 
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S, S, D, window};
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -60,6 +65,8 @@ int swa_sink_decode(const void *q, const void *kcache, const void *vcache, const
         !aligned(sink, 4) || !aligned(lse, 4) || !aligned(cache_len, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || T_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hq * T_q)) return SWA_ERR_SHAPE;
+    if ((long)window * D * 2 > kMaxGridX) return SWA_ERR_UNSUPPORTED;   // one ring's buffer window
 
     swa::DecodeArgs a{q, kcache, vcache, sink, out, lse, cache_len, B, Hq, Hkv, T_q, window, D};
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -85,6 +92,7 @@ int global_sink_attn(const void *q, const void *k, const void *v, const float *s
         !aligned(sink, 4) || !aligned(lse, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
 
     // Every key position is inside the window: window = S_kv.
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
@@ -105,10 +113,10 @@ const char *swa_sink_strerror(int code) {
     case SWA_ERR_NULL: return "a required pointer argument is NULL";
     case SWA_ERR_SHAPE:
         return "invalid sizes (negative size, Hq % Hkv != 0, window < 1, T_q > window, "
-               "S_q > S_kv, or batch/heads above 65535)";
+               "S_q > S_kv, batch/heads above 65535, or more work units than one launch holds)";
     case SWA_ERR_UNSUPPORTED:
-        return "unsupported argument (head dim not 64/128, unknown dtype, or a pointer "
-               "not aligned to 16 bytes)";
+        return "unsupported argument (head dim not 64/128, unknown dtype, a pointer not "
+               "aligned to 16 bytes, or a ring cache above 2 GiB per (sequence, KV head))";
     case SWA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case SWA_ERR_HIP: return "the HIP runtime reported an error when launching";
     default: return "unknown status code";

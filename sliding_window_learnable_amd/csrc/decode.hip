@@ -341,13 +341,15 @@ SplitPlan plan_split(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {
     const int G = Hq / Hkv;
     const int n_ct = (G * S_q + 31) / 32;
     const int ck = kChunk;
-    (void)D;
     const long pairs = (long)B * Hkv * n_ct;
     const int max_splits = (S_kv + ck - 1) / ck;
     int want = (int)((kSplitTargetWaves + pairs - 1) / pairs);
     want = max(1, min(want, max_splits));
     int kps = (S_kv + want - 1) / want;
     kps = ((kps + ck - 1) / ck) * ck;
+    // Each split's buffer window (kps rows of all KV heads) stays below 2^31 bytes.
+    const long cap = ((1L << 31) / ((long)Hkv * D * 2)) / ck * ck;
+    if (kps > cap) kps = (int)cap;
     const int n_splits = (S_kv + kps - 1) / kps;
     return {n_splits, kps, n_ct};
 }

@@ -29,8 +29,9 @@ struct DecodeArgs {
     int B, Hq, Hkv, T, W, D;
 };
 
-// bf16 sliding-window prefill, LDS ring of key tiles (window <= 129).
+// bf16 sliding-window prefill, LDS ring of key tiles (98 <= window <= 129).
 bool prefill_ring_supported(int window, int G);
+int prefill_chunk_cap(int Hq, int Hkv, int D, int ntw);
 hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream);
 
 // bf16 banded / causal attention streaming key tiles through LDS: any window,

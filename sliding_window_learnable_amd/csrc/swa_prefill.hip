@@ -140,10 +140,12 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const int r0 = kTile * T_first;
     const rsrc_t qr = make_rsrc(q + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
     const rsrc_t orr = make_rsrc(out + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
-    const rsrc_t kr = make_rsrc(k + (((size_t)b * S + r0) * Hkv + g) * D, (S - r0) * rs);
-    const rsrc_t vr = make_rsrc(v + (((size_t)b * S + r0) * Hkv + g) * D, (S - r0) * rs);
-    const rsrc_t lr = make_rsrc(lse != nullptr ? lse + ((size_t)b * Hq + h) * S : nullptr,
-                                lse != nullptr ? (uint32_t)S * 4 : 0u);
+    // K/V rows [r0, c1): every row this chunk uses (the prefetch past the
+    // chunk's last tile reads zeros and is never stored).
+    const rsrc_t kr = make_rsrc(k + (((size_t)b * S + r0) * Hkv + g) * D, (c1 - r0) * rs);
+    const rsrc_t vr = make_rsrc(v + (((size_t)b * S + r0) * Hkv + g) * D, (c1 - r0) * rs);
+    const rsrc_t lr = make_rsrc(lse != nullptr ? lse + ((size_t)b * Hq + h) * S + c0 : nullptr,
+                                lse != nullptr ? (uint32_t)(c1 - c0) * 4 : 0u);
     // QK contraction order: lane half hl feeds dims [64hl, 64hl + 64), the
     // ks-th MFMA step dims 64hl + 8ks .. +8, so each lane reads one whole
     // 128-byte line of its query row (K fragments use the same order).
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             asm volatile("" ::: "memory");             // next half's writes after these reads
         }
         buf_store_f32(l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY, lr, l_lane,
-                      (uint32_t)p0 * 4);
+                      (uint32_t)(p0 - c0) * 4);
 
         if (p0 + kTile < c1) st.store(sm, (T1 + 1) % R, tid);
     };
@@ -352,6 +354,21 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     }
 }
 
+}  // namespace
+
+// Largest chunk (a multiple of 32 positions) whose buffer windows stay below
+// 2^31 bytes: q/out rows [c0, c1) of all heads, k/v rows [r0, c1) of one KV
+// head including the (ntw-1)-tile halo.
+int prefill_chunk_cap(int Hq, int Hkv, int D, int ntw) {
+    const long limit = 1L << 31;
+    const long q_rows = limit / ((long)Hq * D * 2);
+    const long kv_rows = limit / ((long)Hkv * D * 2) - (long)kTile * (ntw - 1);
+    const long rows = q_rows < kv_rows ? q_rows : kv_rows;
+    return (int)(rows < kTile ? kTile : (rows / kTile) * kTile);
+}
+
+namespace {
+
 template <int D, int NW>
 hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
     const int tiles = (a.S + kTile - 1) / kTile;
@@ -361,9 +378,9 @@ hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
     per_group = max(1, min(per_group, tiles));
     int steps = (tiles + per_group - 1) / per_group;
     steps = max(steps, min(4, tiles));
-    const int chunk = steps * kTile;
-    const int nchunks = (a.S + chunk - 1) / chunk;
     const int ntw = (a.window - 1 + kTile - 1) / kTile + 1;
+    const int chunk = min(steps * kTile, prefill_chunk_cap(a.Hq, a.Hkv, a.D, ntw));
+    const int nchunks = (a.S + chunk - 1) / chunk;
     dim3 grid(nchunks, a.Hkv, a.B);
     hipLaunchKernelGGL((swa_prefill_ring_kernel<D, NW>), grid, dim3(NW * 64), 0, stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,

@@ -86,6 +86,8 @@ def gattn(lib, q=P, k=P, v=P, sink=P, out=P, lse=None, B=1, Hq=8, Hkv=1, Sq=4, S
     (dict(dtype=2), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=-1), _lib.SWA_ERR_UNSUPPORTED),
     (dict(q=P + 8), _lib.SWA_ERR_UNSUPPORTED), (dict(out=P + 2), _lib.SWA_ERR_UNSUPPORTED),
     (dict(lse=P + 2), _lib.SWA_ERR_UNSUPPORTED),
+    # more 32-row work units than one launch grid holds
+    (dict(B=60000, Hq=64, Hkv=8, S=1 << 30), _lib.SWA_ERR_SHAPE),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
@@ -109,6 +111,8 @@ def test_empty_inputs_are_noops(lib):
     (dict(T=-1), _lib.SWA_ERR_SHAPE), (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE),
     (dict(D=32), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=7), _lib.SWA_ERR_UNSUPPORTED),
     (dict(cache_len=P + 1), _lib.SWA_ERR_UNSUPPORTED), (dict(kc=P + 4), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(B=65535, Hq=65535, Hkv=1, T=1), _lib.SWA_ERR_SHAPE),       # B*Hq*T_q > 2^31-1
+    (dict(W=(1 << 23) + 1, D=128), _lib.SWA_ERR_UNSUPPORTED),       # one ring above 2 GiB
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
@@ -119,6 +123,7 @@ def test_decode_rejects(lib, kw, code):
     (dict(Sq=65, Skv=64), _lib.SWA_ERR_SHAPE), (dict(Skv=-1), _lib.SWA_ERR_SHAPE),
     (dict(Hq=5, Hkv=2), _lib.SWA_ERR_SHAPE),
     (dict(D=100), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=3), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(B=4, Hq=64, Hkv=8, Sq=1 << 30, Skv=1 << 30), _lib.SWA_ERR_SHAPE),
 ])
 def test_global_rejects(lib, kw, code):
     assert gattn(lib, **kw) == code
@@ -131,6 +136,11 @@ def test_global_workspace_checked(lib):
     assert gattn(lib, B=8, Hq=64, Hkv=8, Sq=1, Skv=262144, ws=None, wsb=0) == _lib.SWA_ERR_WORKSPACE
     assert gattn(lib, B=8, Hq=64, Hkv=8, Sq=1, Skv=262144, ws=P, wsb=need - 1) == \
         _lib.SWA_ERR_WORKSPACE
+    # a split's key range stays below 2 GiB of K rows: B=256 sequences fill the
+    # GPU without splitting, but 2M-token caches (4 GiB of K per sequence) are
+    # cut in two: 2 splits x 256 x 64 heads x 1 row x (128 + 2) floats
+    assert lib.global_sink_attn_workspace_bytes(256, 64, 8, 1, 1 << 21, 128) == 2 * 256 * 64 * 130 * 4
+    assert lib.global_sink_attn_workspace_bytes(256, 64, 8, 1, 1 << 20, 128) == 1 * 256 * 64 * 130 * 4
     # invalid sizes report no workspace
     assert lib.global_sink_attn_workspace_bytes(8, 64, 8, 5, 4, 128) == 0
     assert lib.global_sink_attn_workspace_bytes(8, 64, 8, 1, 4096, 96) == 0
