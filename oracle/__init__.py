@@ -14,7 +14,8 @@ numpy arrays into contiguous float64 buffers, and states each call's key set:
 * global causal attention -- with S_q queries at the end of S_kv keys, row i
   sits at position S_kv - S_q + i and sees 0 .. that position (same digest,
   混合注意力机制: global layers see the whole sequence);
-* ring decode -- see ``ring_decode``.
+* ring decode -- see ``ring_decode``;
+* the gradients of the first two -- see ``attend_backward``.
 
 The sink term is described in the same digest, 前置知识 / 注意力sink偏置.
 """
@@ -56,6 +57,9 @@ def bind(path: str):
     lib.oracle_ring_decode.argtypes = [dp, dp, dp, dp, ip, dp, dp,
                                        i64, i64, i64, i64, i64, i64]
     lib.oracle_ring_decode.restype = None
+    lib.oracle_attend_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                           i64, i64, i64, i64, i64, i64]
+    lib.oracle_attend_backward.restype = None
     lib.oracle_count_window_pairs.argtypes = [i64, i64]
     lib.oracle_count_window_pairs.restype = i64
     lib.oracle_threads.argtypes = []
@@ -175,6 +179,26 @@ def ring_decode(q, kcache, vcache, sink, cache_len=None):
     _load().oracle_ring_decode(_dp(q), _dp(kcache), _dp(vcache), _dp(sink), _ip(cl),
                                _dp(out), _dp(lse), B, T, Hq, Hkv, W, D)
     return out, lse
+
+
+def attend_backward(q, k, v, sink, dout, window, lib=None):
+    """Gradients of causal sliding-window attention with a sink (window >= S:
+    global causal attention) for the upstream gradient ``dout``.
+
+    q, dout [B, S, Hq, D]; k, v [B, S, Hkv, D]; sink [Hq]
+    -> dq [B, S, Hq, D], dk, dv [B, S, Hkv, D], dsink [Hq] (float64; dsink
+    summed over the batch).  ``lib`` lets tests run a modified copy."""
+    q, k, v, sink, dout = _f64(q), _f64(k), _f64(v), _f64(sink), _f64(dout)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    dsink = np.empty(Hq)
+    (lib or _load()).oracle_attend_backward(
+        _dp(q), _dp(k), _dp(v), _dp(sink), _dp(dout), _dp(dq), _dp(dk), _dp(dv), _dp(dsink),
+        B, S, Hq, Hkv, D, int(min(window, S)))
+    return dq, dk, dv, dsink
 
 
 def count_window_pairs(S: int, W: int) -> int:

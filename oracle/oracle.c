@@ -175,6 +175,114 @@ void oracle_ring_decode(const double *q, const double *kc, const double *vc,
     }
 }
 
+/*
+ * Gradients of causal sliding-window (or, with W >= S, global causal)
+ * attention with a sink, for an upstream gradient dout.  The sink s_h is a
+ * learnable per-head parameter (technical-report digest, 前置知识 /
+ * 注意力sink偏置), so its gradient is part of the result.
+ *
+ *   q, dout, dq [B, S, Hq, D]    k, v, dk, dv [B, S, Hkv, D]
+ *   sink, dsink [Hq]             row i sees positions max(0, i-W+1) .. i
+ *
+ * With the forward of one row written as
+ *   x_j = scale q_i.k_j,  lse = log(e^{s_h} + sum_j e^{x_j}),
+ *   P_j = e^{x_j - lse},  p_sink = e^{s_h - lse},  out_i = sum_j P_j v_j
+ * and L = sum over rows and heads of dout_i . out_i, the chain rule gives
+ *   dv_j  += P_j dout_i
+ *   dP_j   = dout_i . v_j
+ *   Dsum   = sum_j P_j dP_j         (the sink's value vector is zero)
+ *   dx_j   = P_j (dP_j - Dsum)
+ *   ds_h  += p_sink (0 - Dsum)
+ *   dq_i  += scale dx_j k_j,    dk_j += scale dx_j q_i
+ * Every row's forward is recomputed from the definition; dk and dv sum over
+ * the query heads that share a KV head, dsink over sequences and rows.
+ */
+void oracle_attend_backward(const double *q, const double *k, const double *v,
+                            const double *sink, const double *dout, double *dq,
+                            double *dk, double *dv, double *dsink, int64_t B,
+                            int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                            int64_t W)
+{
+    const int64_t G = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    double *ds_part = (double *)calloc((size_t)(B * Hq), sizeof(double));
+    for (int64_t e = 0; e < B * S * Hq * D; ++e)
+        dq[e] = 0.0;
+    for (int64_t e = 0; e < B * S * Hkv * D; ++e) {
+        dk[e] = 0.0;
+        dv[e] = 0.0;
+    }
+#pragma omp parallel
+    {
+        double *x = (double *)malloc((size_t)S * sizeof(double));
+        double *dp = (double *)malloc((size_t)S * sizeof(double));
+        /* (b, g) pairs own disjoint rows of dk, dv and dq: no races. */
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t g = 0; g < Hkv; ++g) {
+                for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                    const double s = sink[h];
+                    for (int64_t i = 0; i < S; ++i) {
+                        const int64_t lo = i - W + 1 > 0 ? i - W + 1 : 0;
+                        const int64_t n = i - lo + 1;
+                        const double *qi = q + ((b * S + i) * Hq + h) * D;
+                        const double *gi = dout + ((b * S + i) * Hq + h) * D;
+                        /* forward of the row: scores, max, log-sum-exp */
+                        double M = s;
+                        for (int64_t j = 0; j < n; ++j) {
+                            const double *kj = k + ((b * S + lo + j) * Hkv + g) * D;
+                            double dot = 0.0;
+                            for (int64_t d = 0; d < D; ++d)
+                                dot += qi[d] * kj[d];
+                            x[j] = scale * dot;
+                            if (x[j] > M)
+                                M = x[j];
+                        }
+                        double Z = 0.0;
+                        for (int64_t j = 0; j < n; ++j)
+                            Z += exp(x[j] - M);
+                        const double E = isinf(s) && s < 0 ? 0.0 : exp(s - M);
+                        const double lse = M + log(Z + E);
+                        /* dP_j = dout_i . v_j and Dsum = sum_j P_j dP_j */
+                        double Dsum = 0.0;
+                        for (int64_t j = 0; j < n; ++j) {
+                            const double *vj = v + ((b * S + lo + j) * Hkv + g) * D;
+                            double dot = 0.0;
+                            for (int64_t d = 0; d < D; ++d)
+                                dot += gi[d] * vj[d];
+                            dp[j] = dot;
+                            Dsum += exp(x[j] - lse) * dot;
+                        }
+                        const double p_sink = isinf(s) && s < 0 ? 0.0 : exp(s - lse);
+                        ds_part[b * Hq + h] += p_sink * (0.0 - Dsum);
+                        double *dqi = dq + ((b * S + i) * Hq + h) * D;
+                        for (int64_t j = 0; j < n; ++j) {
+                            const double P = exp(x[j] - lse);
+                            const double dx = P * (dp[j] - Dsum);
+                            const int64_t row = (b * S + lo + j) * Hkv + g;
+                            const double *kj = k + row * D;
+                            for (int64_t d = 0; d < D; ++d) {
+                                dv[row * D + d] += P * gi[d];
+                                dk[row * D + d] += scale * dx * qi[d];
+                                dqi[d] += scale * dx * kj[d];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(x);
+        free(dp);
+    }
+    for (int64_t h = 0; h < Hq; ++h) {
+        double t = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            t += ds_part[b * Hq + h];
+        dsink[h] = t;
+    }
+    free(ds_part);
+}
+
 /* Number of (query, key) pairs a causal window-W layer attends over S tokens:
  * enumerated one row at a time (used to check closed-form FLOP counts). */
 int64_t oracle_count_window_pairs(int64_t S, int64_t W)

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_backward as bwd
 from tests import test_oracle_pins as pins
 
 MUTANTS = {
@@ -32,6 +33,18 @@ MUTANTS = {
     "ring keeps one key too few": ("const int64_t oldest = L - W > 0 ? L - W : 0;",
                                    "const int64_t oldest = L - W + 1 > 0 ? L - W + 1 : 0;"),
     "pair count misses the diagonal": ("total += i - lo + 1;", "total += i - lo;"),
+    # backward
+    "backward drops -Dsum": ("const double dx = P * (dp[j] - Dsum);", "const double dx = P * dp[j];"),
+    "dk misses the scale": ("dk[row * D + d] += scale * dx * qi[d];",
+                            "dk[row * D + d] += dx * qi[d];"),
+    "sink gradient sign flipped": ("ds_part[b * Hq + h] += p_sink * (0.0 - Dsum);",
+                                   "ds_part[b * Hq + h] += p_sink * Dsum;"),
+    "dv weighted by dP": ("dv[row * D + d] += P * gi[d];", "dv[row * D + d] += dp[j] * gi[d];"),
+    "backward lse drops the sink": ("const double lse = M + log(Z + E);",
+                                    "const double lse = M + log(Z);"),
+    "dq uses q": ("dqi[d] += scale * dx * kj[d];", "dqi[d] += scale * dx * qi[d];"),
+    "backward misses the diagonal key": ("const int64_t n = i - lo + 1;",
+                                         "const int64_t n = i - lo;"),
 }
 
 PINS = [
@@ -50,6 +63,13 @@ PINS = [
     (pins.test_ring_decode_full_ring_matches_prefill_and_is_slot_order_free, {}),
     (pins.test_ring_decode_draft_windows, {}),
     (pins.test_window_pair_count_closed_form, dict(S=5000, W=128)),
+    (bwd.test_backward_equals_autograd, dict(W=9)),
+    (bwd.test_backward_equals_autograd_gqa_shapes, {}),
+    (bwd.test_sink_neg_inf_has_zero_gradient, {}),
+    (bwd.test_backward_matches_finite_differences, {}),
+    (bwd.test_gqa_is_repeated_kv_heads_summed, {}),
+    (bwd.test_sink_gradient_from_forward_outputs, dict(W=3)),
+    (bwd.test_dv_is_attention_weights_times_dout, {}),
 ]
 
 
