@@ -139,6 +139,38 @@ SWA_API int global_sink_attn(const void *q, const void *k, const void *v, const 
                      int D, void *workspace, size_t workspace_bytes, int dtype,
                      void *stream);
 
+/*
+ * Gradients of swa_sink_prefill (window < S) or of causal global attention
+ * with a sink (window >= S, S_q == S_kv == S) for an upstream gradient dout:
+ * dq, dk, dv and the gradient of the learnable sink.
+ * Source: technical-report digest, 前置知识 / 注意力sink偏置 (the sink is a
+ * learnable per-head term of every softmax denominator, i.e. a virtual key
+ * with logit s_h and no value); window and causality as for the forward.
+ *
+ *   q, out, dout, dq [B, S, Hq, D]    k, v, dk, dv [B, S, Hkv, D]
+ *   sink, dsink [Hq] (float32)        lse [B, Hq, S] (float32)
+ *
+ * `out` and `lse` are the forward's outputs for the same inputs.  With
+ * P_ij = e^{x_ij - lse_i} and D_i = dout_i . out_i:
+ *   dv_j = sum_i P_ij dout_i,   dx_ij = P_ij (dout_i . v_j - D_i),
+ *   dq_i = sum_j dx_ij k_j / sqrt(D),   dk_j = sum_i dx_ij q_i / sqrt(D),
+ *   dsink_h = -sum_{b,i} e^{s_h - lse_i} D_i     (summed over the batch).
+ * dk/dv sum over the query heads of a KV head.  dq, dk, dv (dtype) and dsink
+ * are overwritten, not accumulated.  The bf16 path computes in float32 from
+ * bf16 operands and rounds the gradients to bf16 (RNE).
+ *
+ * `workspace`: device memory of at least
+ * swa_sink_backward_workspace_bytes(B, Hq, S) bytes, 16-byte aligned
+ * (SWA_ERR_WORKSPACE if missing or too small); its contents are scratch.
+ * The result is deterministic: no atomics, fixed reduction order.
+ */
+SWA_API size_t swa_sink_backward_workspace_bytes(int B, int Hq, int S);
+SWA_API int swa_sink_backward(const void *q, const void *k, const void *v, const float *sink,
+                              const void *out, const float *lse, const void *dout, void *dq,
+                              void *dk, void *dv, float *dsink, int B, int Hq, int Hkv, int S,
+                              int D, int window, void *workspace, size_t workspace_bytes,
+                              int dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 SWA_API const char *swa_sink_strerror(int code);
 

@@ -7,7 +7,8 @@ plumbing), pass raw pointers plus the current HIP stream, and raise on a
 non-zero status.  Every step of the computation runs in the HIP kernels.
 
 Names follow the C entry points: ``swa_sink_prefill``, ``swa_sink_decode``,
-``global_sink_attn`` (plus ``global_sink_attn_workspace_bytes``).
+``global_sink_attn`` (plus ``global_sink_attn_workspace_bytes``) and the
+backward ``swa_sink_backward`` (plus ``swa_sink_backward_workspace_bytes``).
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ __all__ = [
     "swa_sink_decode",
     "global_sink_attn",
     "global_sink_attn_workspace_bytes",
+    "swa_sink_backward",
+    "swa_sink_backward_workspace_bytes",
     "SwaError",
 ]
 
@@ -142,3 +145,39 @@ def global_sink_attn(q, k, v, sink, out=None, lse=None, workspace=None, want_lse
           _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, D, _ptr(workspace), wbytes,
           dt, _stream(stream))
     return out, lse
+
+
+def swa_sink_backward_workspace_bytes(B, Hq, S) -> int:
+    return int(_lib.load().swa_sink_backward_workspace_bytes(B, Hq, S))
+
+
+def swa_sink_backward(q, k, v, sink, out, lse, dout, window, dq=None, dk=None, dv=None,
+                      dsink=None, workspace=None, stream=None):
+    """Gradients of swa_sink_prefill (window < S) or of causal global attention
+    (window >= S) for the upstream gradient ``dout``.
+
+    q, out, dout [B, S, Hq, D]; k, v [B, S, Hkv, D]; sink [Hq]; lse [B, Hq, S]
+    (the forward's outputs).  Returns (dq, dk, dv, dsink) with dsink [Hq]
+    float32 summed over the batch.
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if (k.shape != (B, S, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,)
+            or out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, S)):
+        raise ValueError("shape mismatch")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dsink is None:
+        dsink = torch.empty((Hq,), device=q.device, dtype=torch.float32)
+    need = swa_sink_backward_workspace_bytes(B, Hq, S)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_device(q, k, v, sink, out, lse, dout, dq, dk, dv, dsink, workspace)
+    dt = _dtype_code(q, k, v, out, dout, dq, dk, dv)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call(_lib.load().swa_sink_backward, "swa_sink_backward", _ptr(q), _ptr(k), _ptr(v),
+          _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(dsink), B, Hq, Hkv, S, D, int(window), _ptr(workspace), wbytes, dt,
+          _stream(stream))
+    return dq, dk, dv, dsink

@@ -19,6 +19,8 @@ EXPORTS = (
     "swa_sink_decode",
     "global_sink_attn_workspace_bytes",
     "global_sink_attn",
+    "swa_sink_backward_workspace_bytes",
+    "swa_sink_backward",
     "swa_sink_strerror",
 )
 
@@ -50,6 +52,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.global_sink_attn_workspace_bytes.restype = sz
     lib.global_sink_attn.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, sz, i, vp]
     lib.global_sink_attn.restype = i
+    lib.swa_sink_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.swa_sink_backward_workspace_bytes.restype = sz
+    lib.swa_sink_backward.argtypes = [vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
+                                      i, i, i, i, i, i, vp, sz, i, vp]
+    lib.swa_sink_backward.restype = i
     lib.swa_sink_strerror.argtypes = [i]
     lib.swa_sink_strerror.restype = ctypes.c_char_p
     if path == LIB_PATH:

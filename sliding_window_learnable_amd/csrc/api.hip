@@ -107,6 +107,38 @@ int global_sink_attn(const void *q, const void *k, const void *v, const float *s
     return status_of(swa::launch_stream_bf16(a, st));
 }
 
+size_t swa_sink_backward_workspace_bytes(int B, int Hq, int S) {
+    if (B < 1 || Hq < 1 || S < 1) return 0;
+    return swa::backward_workspace_bytes(B, Hq, S);
+}
+
+int swa_sink_backward(const void *q, const void *k, const void *v, const float *sink,
+                      const void *out, const float *lse, const void *dout, void *dq, void *dk,
+                      void *dv, float *dsink, int B, int Hq, int Hkv, int S, int D, int window,
+                      void *workspace, size_t workspace_bytes, int dtype, void *stream) {
+    if (!q || !k || !v || !sink || !out || !lse || !dout || !dq || !dk || !dv || !dsink)
+        return SWA_ERR_NULL;
+    if (S < 0 || window < 1) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4) || !aligned(dsink, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hq * S)) return SWA_ERR_SHAPE;
+    const size_t need = swa::backward_workspace_bytes(B, Hq, S);
+    if (workspace == nullptr || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return SWA_ERR_UNSUPPORTED;
+
+    float *ws = static_cast<float *>(workspace);
+    swa::BackwardArgs a{q, k, v, sink, out, lse, dout, dq, dk, dv, dsink,
+                        ws, ws + (size_t)B * Hq * S, B, Hq, Hkv, S, D, window < S ? window : S};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_backward_f32(a, st));
+    return status_of(swa::launch_backward_bf16(a, st));
+}
+
 const char *swa_sink_strerror(int code) {
     switch (code) {
     case SWA_OK: return "success";

@@ -47,6 +47,23 @@ bool splitkv_preferred(int Hq, int Hkv, int S_q, int S_kv);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
 hipError_t launch_splitkv_bf16(const PrefillArgs &a, void *workspace, hipStream_t stream);
 
+// Backward of causal sliding-window / global attention with a sink.
+struct BackwardArgs {
+    const void *q, *k, *v;
+    const float *sink;
+    const void *out;            // forward output
+    const float *lse;           // forward lse [B, Hq, S]
+    const void *dout;
+    void *dq, *dk, *dv;
+    float *dsink;
+    float *ws_dsum;             // [B, Hq, S]: D_i = dO_i . O_i
+    float *ws_part;             // [B, Hq, ceil(S/32)]: sink-gradient partials
+    int B, Hq, Hkv, S, D, window;
+};
+size_t backward_workspace_bytes(int B, int Hq, int S);
+hipError_t launch_backward_f32(const BackwardArgs &a, hipStream_t stream);
+hipError_t launch_backward_bf16(const BackwardArgs &a, hipStream_t stream);
+
 // float32 path (one wavefront per query row and head), every call type.
 hipError_t launch_generic_f32_linear(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_generic_f32_ring(const DecodeArgs &a, hipStream_t stream);

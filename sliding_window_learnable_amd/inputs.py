@@ -4,7 +4,8 @@ This module holds no attention arithmetic: it only draws Gaussian tensors of
 the workload shapes from explicitly seeded generators, so that the HIP path
 and the CPU oracle see identical values.
 
-Seed recipe: ``1000*config + 10*layer + {q: 1, k: 2, v: 3, sink: 4}``, with
+Seed recipe: ``1000*config + 10*layer + {q: 1, k: 2, v: 3, sink: 4, dout: 5}``
+(dout: the upstream gradient of a backward pass), with
 the workload configs numbered 1..5 (tiny reference, 32K prefill, batched
 decode, hybrid 5:1 stack, long context).  Values are drawn in float32 with
 ``torch.randn`` and rounded to bfloat16 (round-to-nearest-even) when the
@@ -14,7 +15,7 @@ from __future__ import annotations
 
 import torch
 
-TENSOR_SEED = {"q": 1, "k": 2, "v": 3, "sink": 4}
+TENSOR_SEED = {"q": 1, "k": 2, "v": 3, "sink": 4, "dout": 5}
 
 
 def seed_for(config: int, layer: int, tensor: str) -> int:
@@ -38,6 +39,12 @@ def attention_inputs(config: int, layer: int, B: int, S_q: int, S_kv: int, Hq: i
     v = randn((B, S_kv, Hkv, D), seed_for(config, layer, "v"), dtype, device)
     sink = randn((Hq,), seed_for(config, layer, "sink"), torch.float32, device)
     return q, k, v, sink
+
+
+def upstream_grad(config: int, layer: int, B: int, S: int, Hq: int, D: int,
+                  dtype=torch.bfloat16, device="cpu"):
+    """dout [B, S, Hq, D] in ``dtype``: the gradient arriving at the attention output."""
+    return randn((B, S, Hq, D), seed_for(config, layer, "dout"), dtype, device)
 
 
 def ring_inputs(config: int, layer: int, B: int, T: int, Hq: int, Hkv: int, W: int,

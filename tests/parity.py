@@ -6,6 +6,14 @@ Bars (stated once, used everywhere):
 * lse (natural log, sink included): <= 1e-5 (float32) / 1e-3 (bfloat16).
   Scores of bf16 inputs are exact products summed in fp32, so the row
   log-sum-exp is far tighter than the bf16-rounded output.
+* gradients (dq, dk, dv; dsink), relative to the tensor's scale:
+  |gpu - oracle| <= c (rms(oracle) + |oracle|) elementwise, with
+  c = 1e-4 (float32) and, for bfloat16 inputs, c = 5e-2 for dq/dk/dv and
+  1e-2 for dsink.  With bf16 inputs the backward takes the forward's
+  bf16-rounded output O for D_i = dO.O, and dq/dk depend on the difference
+  dP - D_i; the rounding of O (and of P, dS as bf16 MFMA operands) shows up
+  there at a few percent of the gradient's scale, against errors of order
+  the scale itself for a wrong or missing term.
 """
 from __future__ import annotations
 
@@ -15,6 +23,8 @@ import torch
 OUT_F32_ATOL = 1e-5
 OUT_BF16_ATOL, OUT_BF16_RTOL = 2e-2, 1e-2
 LSE_ATOL = {torch.float32: 1e-5, torch.bfloat16: 1e-3}
+GRAD_C = {torch.float32: 1e-4, torch.bfloat16: 5e-2}
+DSINK_C = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -47,4 +57,21 @@ def check_lse(gpu, ref, dtype, what="lse"):
     worst = float(np.nanmax(err)) if err.size else 0.0
     assert not np.isnan(err).any() and worst <= LSE_ATOL[dtype], \
         "%s: max abs err %.3g > %.1g" % (what, worst, LSE_ATOL[dtype])
+    return worst
+
+
+def check_grad(gpu, ref, dtype, what, c=None):
+    """|gpu - ref| <= c (rms(ref) + |ref|) elementwise (see the module notes)."""
+    g = to64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.isfinite(g).all(), "%s has non-finite values" % what
+    if c is None:
+        c = DSINK_C[dtype] if what == "dsink" else GRAD_C[dtype]
+    rms = float(np.sqrt((r ** 2).mean())) if r.size else 0.0
+    err = np.abs(g - r)
+    ratio = err / (rms + np.abs(r) + 1e-30)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= c, "%s: max err/(rms+|ref|) %.3g > %.1g (max abs err %.3g, rms %.3g)" % (
+        what, worst, c, float(err.max()), rms)
     return worst

@@ -153,3 +153,32 @@ def test_binding_refuses_cpu_tensors():
     k = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         swa.swa_sink_prefill(q, k, k, torch.zeros(8), 128)
+
+
+def bwd(lib, q=P, k=P, v=P, sink=P, out=P, lse=P, dout=P, dq=P, dk=P, dv=P, dsink=P, B=1, Hq=8,
+        Hkv=1, S=16, D=128, window=128, ws=P, wsb=1 << 20, dtype=1):
+    return lib.swa_sink_backward(q, k, v, sink, out, lse, dout, dq, dk, dv, dsink, B, Hq, Hkv, S, D,
+                                 window, ws, wsb, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(lse=None), _lib.SWA_ERR_NULL),
+    (dict(dout=None), _lib.SWA_ERR_NULL), (dict(dk=None), _lib.SWA_ERR_NULL),
+    (dict(dsink=None), _lib.SWA_ERR_NULL), (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(S=-1), _lib.SWA_ERR_SHAPE), (dict(window=0), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE), (dict(B=70000), _lib.SWA_ERR_SHAPE),
+    (dict(D=48), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=9), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(dq=P + 8), _lib.SWA_ERR_UNSUPPORTED), (dict(dsink=P + 2), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(ws=None), _lib.SWA_ERR_WORKSPACE), (dict(wsb=16), _lib.SWA_ERR_WORKSPACE),
+    (dict(ws=P + 4), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_backward_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_backward_workspace_and_empty(lib):
+    # D_i per (b, h, row) plus one sink-gradient partial per 32 rows, float32
+    assert lib.swa_sink_backward_workspace_bytes(2, 64, 1000) == 4 * 2 * 64 * (1000 + 32)
+    assert lib.swa_sink_backward_workspace_bytes(0, 64, 1000) == 0
+    assert bwd(lib, B=0, ws=None, wsb=0) == _lib.SWA_OK
+    assert bwd(lib, S=0, ws=None, wsb=0) == _lib.SWA_OK
