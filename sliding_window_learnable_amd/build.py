@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden", "-ffp-contract=fast", "-fno-strict-aliasing",
     # packed fp32 arithmetic stays off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the AGPR form makes the
+    # compiler copy scores between the two register files every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

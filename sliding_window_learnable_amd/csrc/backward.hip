@@ -12,7 +12,9 @@
 // Passes: (1) bwd_pre: D_i and per-32-row partials of the sink gradient;
 // (2) dsink: the partials of each head summed in a fixed order
 // (deterministic, no atomics); (3) dq and (4) dk/dv, each owning its
-// outputs, so no pass accumulates into another's memory.
+// outputs, so no pass accumulates into another's memory.  This file holds
+// passes 1-2 and the float32 path of 3-4 (one wave per output row); the
+// bf16 MFMA kernels of 3-4 are in backward_mfma.hip.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -224,7 +226,11 @@ hipError_t launch_backward_f32(const BackwardArgs &a, hipStream_t stream) {
     return launch_generic<float>(a, stream);
 }
 
-hipError_t launch_backward_bf16(const BackwardArgs &a, hipStream_t stream) {
+hipError_t launch_backward_pre(const BackwardArgs &a, hipStream_t stream, bool bf16_inputs) {
+    return bf16_inputs ? launch_pre<bf16>(a, stream) : launch_pre<float>(a, stream);
+}
+
+hipError_t launch_backward_bf16_rowwise(const BackwardArgs &a, hipStream_t stream) {
     return launch_generic<bf16>(a, stream);
 }
 

@@ -61,8 +61,11 @@ struct BackwardArgs {
     int B, Hq, Hkv, S, D, window;
 };
 size_t backward_workspace_bytes(int B, int Hq, int S);
+hipError_t launch_backward_pre(const BackwardArgs &a, hipStream_t stream, bool bf16_inputs);
 hipError_t launch_backward_f32(const BackwardArgs &a, hipStream_t stream);
 hipError_t launch_backward_bf16(const BackwardArgs &a, hipStream_t stream);
+// one wave per output row, bf16 in/out (reference-structured; not dispatched)
+hipError_t launch_backward_bf16_rowwise(const BackwardArgs &a, hipStream_t stream);
 
 // float32 path (one wavefront per query row and head), every call type.
 hipError_t launch_generic_f32_linear(const PrefillArgs &a, hipStream_t stream);

@@ -8,12 +8,13 @@ Bars (stated once, used everywhere):
   log-sum-exp is far tighter than the bf16-rounded output.
 * gradients (dq, dk, dv; dsink), relative to the tensor's scale:
   |gpu - oracle| <= c (rms(oracle) + |oracle|) elementwise, with
-  c = 1e-4 (float32) and, for bfloat16 inputs, c = 5e-2 for dq/dk/dv and
-  1e-2 for dsink.  With bf16 inputs the backward takes the forward's
-  bf16-rounded output O for D_i = dO.O, and dq/dk depend on the difference
-  dP - D_i; the rounding of O (and of P, dS as bf16 MFMA operands) shows up
-  there at a few percent of the gradient's scale, against errors of order
-  the scale itself for a wrong or missing term.
+  c = 1e-4 (float32) and, for bfloat16 inputs, c = 8e-2 for dq/dk/dv and
+  1e-2 for dsink.  The bf16 path feeds P and dS to the matrix cores as
+  bf16 (as the forward feeds P), and takes D_i = dO.O from the forward's
+  bf16-rounded O.  Rounding P alone, evaluated exactly in fp64 on the
+  1000-token, 64-head case, already moves dv by up to 2.8e-2 of this scale
+  (the kernels measure 2-4.3e-2); a wrong or missing term moves the result
+  by the order of the scale itself.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ import torch
 OUT_F32_ATOL = 1e-5
 OUT_BF16_ATOL, OUT_BF16_RTOL = 2e-2, 1e-2
 LSE_ATOL = {torch.float32: 1e-5, torch.bfloat16: 1e-3}
-GRAD_C = {torch.float32: 1e-4, torch.bfloat16: 5e-2}
+GRAD_C = {torch.float32: 1e-4, torch.bfloat16: 8e-2}
 DSINK_C = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
 
 
