@@ -132,8 +132,9 @@ int swa_sink_backward(const void *q, const void *k, const void *v, const float *
     if (!aligned(workspace, 16)) return SWA_ERR_UNSUPPORTED;
 
     float *ws = static_cast<float *>(workspace);
-    swa::BackwardArgs a{q, k, v, sink, out, lse, dout, dq, dk, dv, dsink,
-                        ws, ws + (size_t)B * Hq * S, B, Hq, Hkv, S, D, window < S ? window : S};
+    const size_t rows = (size_t)B * Hq * S;
+    swa::BackwardArgs a{q,  k,  v,  sink, out, lse, dout, dq, dk, dv, dsink, ws, ws + rows,
+                        ws + 2 * rows, B, Hq, Hkv, S, D, window < S ? window : S};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == SWA_F32) return status_of(swa::launch_backward_f32(a, st));
     return status_of(swa::launch_backward_bf16(a, st));

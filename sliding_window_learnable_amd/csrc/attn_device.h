@@ -36,6 +36,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// An empty asm that reads x: the compiler waits here for the load that
+// produced x, so no wait for it is left to land inside a later loop (where
+// it would also wait for that loop's own prefetches).
+template <class V>
+__device__ __forceinline__ void retire(const V &x) {
+    asm volatile("" ::"v"(x));
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

@@ -44,8 +44,8 @@ __global__ __launch_bounds__(64) void bwd_pre_kernel(const T *__restrict__ out,
                                                      const T *__restrict__ dout,
                                                      const float *__restrict__ lse,
                                                      const float *__restrict__ sink,
-                                                     float *__restrict__ dsum, float *__restrict__ part,
-                                                     int S, int Hq, int D) {
+                                                     float *__restrict__ dsum, float *__restrict__ l2,
+                                                     float *__restrict__ part, int S, int Hq, int D) {
     constexpr int EPC = 16 / sizeof(T);              // elements per 16-byte piece
     const int LPR = D / EPC;                         // lanes per row (8..32)
     const int RPP = 64 / LPR;                        // rows per pass
@@ -65,6 +65,7 @@ __global__ __launch_bounds__(64) void bwd_pre_kernel(const T *__restrict__ out,
         if (ok && sub == 0) {
             const size_t li = ((size_t)b * Hq + h) * S + i;
             dsum[li] = acc;
+            l2[li] = lse[li] * kLog2e;
             if (s != -INFINITY) term += expf(s - lse[li]) * acc;
         }
     }
@@ -184,8 +185,8 @@ template <class T>
 hipError_t launch_pre(const BackwardArgs &a, hipStream_t stream) {
     const int tiles = (a.S + kRows - 1) / kRows;
     hipLaunchKernelGGL(bwd_pre_kernel<T>, dim3(tiles, a.Hq, a.B), dim3(64), 0, stream,
-                       (const T *)a.out, (const T *)a.dout, a.lse, a.sink, a.ws_dsum, a.ws_part,
-                       a.S, a.Hq, a.D);
+                       (const T *)a.out, (const T *)a.dout, a.lse, a.sink, a.ws_dsum, a.ws_l2,
+                       a.ws_part, a.S, a.Hq, a.D);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dsink_kernel, dim3(a.Hq), dim3(64), 0, stream, a.ws_part, a.dsink, a.B,
@@ -200,7 +201,7 @@ hipError_t launch_generic(const BackwardArgs &a, hipStream_t stream);
 
 size_t backward_workspace_bytes(int B, int Hq, int S) {
     const size_t tiles = (size_t)(S + kRows - 1) / kRows;
-    return 4 * (size_t)B * Hq * ((size_t)S + tiles);
+    return 4 * (size_t)B * Hq * (2 * (size_t)S + tiles);
 }
 
 namespace {

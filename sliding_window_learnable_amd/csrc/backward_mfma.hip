@@ -14,13 +14,16 @@
 //   Per tile: S^T = K Q^T, dP^T = V dO^T (lane = query), P^T, dS^T, and
 //   dQ^T += K^T dS^T.
 // dk/dv: one work-group per (batch, KV head, NW consecutive 32-key tiles),
-//   one wave per key tile; K and V of the wave's tile stay in registers as
-//   the B operands.  The work-group walks every query head of the group and
-//   every 32-row query tile that sees one of its keys, staging Q, dO (rows
-//   and transposed), lse and D once for all its waves.  Per (head, query
-//   tile) a wave computes S = Q K^T and dP = dO V^T (lane = key), P, dS, and
-//   dV^T += dO^T P, dK^T += Q^T dS; dk/dv sum over the heads inside the wave,
-//   so no reduction across waves or work-groups is needed.
+//   two waves per key tile: an S wave (S = Q K^T, P, dV^T += dO^T P; K in
+//   registers) and a dP wave (dP = dO V^T, dS = P (dP - D) with P handed
+//   over through LDS, dK^T += Q^T dS; V in registers).  The work-group walks
+//   every query head of the group and every 32-row query tile that sees one
+//   of its keys; Q, dO, lse and D of each (head, query tile) are copied
+//   from memory straight into LDS three steps ahead, in rows whose 16-byte
+//   chunks are swizzled so that both the row reads (A of S and dP) and the
+//   transposing reads (A of dK^T and dV^T) are free of bank conflicts.
+//   dk/dv sum over the heads inside the wave, so no reduction across waves
+//   or work-groups is needed.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -165,6 +168,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
         f32x16 acc[D / 32];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            retire(qf[ks]);
+            retire(gf[ks]);
+        }
 
         for (int t = 0; t < n_tiles; ++t) {
             const int T = T_lo + t, slot = t & 1;
@@ -218,90 +226,90 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 
 // ========================================================================= dk/dv
 
+// Q and dO tiles are unpadded rows whose 16-byte chunks are XOR-swizzled by
+// row (chunk c of row r sits at c ^ swz(r)), so that both the row reads of
+// S and dP (16 rows, one chunk) and the transposing reads of dK and dV
+// (4 rows x 32 dims per 32 lanes) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane j supplies the address of
+// 4 bf16 (row j/4, dims 4(j%4)..+3 of a 16-dim span); lane i receives the
+// element at dim i of each of the 4 rows.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Buffer descriptor as four scalar dwords (raw buffer, num_records bytes).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
+    const unsigned long long p = (unsigned long long)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+    r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// Buffer -> LDS copy (no registers): lane l's 16 bytes at voff land at
+// lds + 16 l; out-of-range dwords land as zero.  Written as asm so that the
+// compiler does not wait for every copy before each LDS read (it cannot
+// tell the copies' targets from the tiles being read); the copies are
+// waited for explicitly (vmcnt) before the barrier that publishes them.
+// m0 is reserved to the compiler, which uses it for nothing in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
+    const unsigned la = __builtin_amdgcn_readfirstlane(
+        (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(la),
+                 "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+constexpr int kKvSlots = 4;     // staging slots: pairs n, n+1 in use, n+2 landed, n+3 in flight
+
 template <int D, int NW>
 struct KvSmem {
-    bf16 kw[NW][kTile][D + 8];  // each wave's K rows: B of S = Q K^T
-    bf16 vw[NW][kTile][D + 8];  // each wave's V rows: B of dP = dO V^T
-    bf16 q[2][kTile][D + 8];    // Q rows: A of S = Q K^T
-    bf16 g[2][kTile][D + 8];    // dO rows: A of dP = dO V^T
-    bf16 qt[2][D][kTile + 8];   // Q^T: A of dK^T = Q^T dS
-    bf16 gt[2][D][kTile + 8];   // dO^T: A of dV^T = dO^T P
-    float l2[2][kTile];         // lse * log2(e); +inf past the end (P = 0)
-    float dd[2][kTile];         // D_i
+    bf16 q[kKvSlots][kTile][D];     // Q rows (swizzled): A of S = Q K^T, read transposed for dK
+    bf16 g[kKvSlots][kTile][D];     // dO rows (swizzled): A of dP = dO V^T, transposed for dV
+    float l2[kKvSlots][kTile];      // lse * log2(e) (0 past the end, where dO = 0)
+    float dd[kKvSlots][kTile];      // D_i
+    f32x4 px[2][NW][4][64];         // P of each key tile, from its S wave to its dP wave
 };
 
-// One (head, 32-row query tile) of Q and dO as 4-row x 8-dim quads plus the
-// rows' lse and D, loaded into registers, then written to an LDS buffer as
-// rows and transposed.
-template <int D, int NT>
-struct KvStager {
-    static constexpr int CH = D / 8;
-    static constexpr int QPT = (2 * 8 * CH + NT - 1) / NT;  // Q and dO quads per thread
-    bf16x8 quad[QPT][4];
-    float l2, dd;
-
-    __device__ __forceinline__ void load(const bf16 *q, const bf16 *dout, const float *lse,
-                                         const float *dsum, int b, int h, int r0, int S, int Hq,
-                                         int tid) {
-        const int rows = min(kTile, S - r0);
-        const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
-        const uint32_t bytes = (uint32_t)(rows - 1) * qrow_bytes + D * 2;
-        const size_t base = (((size_t)b * S + r0) * Hq + h) * D;
-        const rsrc_t qr = make_rsrc(q + base, bytes);
-        const rsrc_t gr = make_rsrc(dout + base, bytes);
-#pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int item = tid + u * NT;
-            if (item < 2 * 8 * CH) {                        // wave-uniform
-                const int it = item % (8 * CH), kq = it & 7, ch = it >> 3;
-                // Q or dO: the same for the whole wave (64-aligned item ranges),
-                // stated so that the descriptor stays scalar.
-                const bool is_q = __builtin_amdgcn_readfirstlane(item / (8 * CH)) == 0;
-                const rsrc_t r = is_q ? qr : gr;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) quad[u][j] = buf_load16(r, (4 * kq + j) * qrow_bytes + 16 * ch, 0);
-            }
-        }
-        if (tid < kTile) {
-            const bool ok = tid < rows;
-            const size_t li = ((size_t)b * Hq + h) * S + r0 + (ok ? tid : 0);
-            l2 = ok ? lse[li] * kLog2e : INFINITY;
-            dd = ok ? dsum[li] : 0.0f;
-        }
-    }
-
-    template <class Smem>
-    __device__ __forceinline__ void store(Smem &sm, int buf, int tid) const {
-#pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int item = tid + u * NT;
-            if (item < 2 * 8 * CH) {
-                const bool is_q = __builtin_amdgcn_readfirstlane(item / (8 * CH)) == 0;
-                const int it = item % (8 * CH), kq = it & 7, ch = it >> 3;
-                bf16(*rws)[D + 8] = is_q ? sm.q[buf] : sm.g[buf];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) *(bf16x8 *)&rws[4 * kq + j][8 * ch] = quad[u][j];
-                lds_settle(quad[u]);
-                store_transposed(is_q ? sm.qt[buf] : sm.gt[buf], quad[u], ch, 4 * kq);
-            }
-        }
-        if (tid < kTile) {
-            sm.l2[buf][tid] = l2;
-            sm.dd[buf][tid] = dd;
-        }
-    }
+template <int V>
+struct IntC {
+    static constexpr int value = V;
 };
 
+// NW key tiles per work-group, two waves per tile: waves 0..NW-1 compute
+// S = Q K^T, P and dV^T += dO^T P (K in registers); waves NW..2NW-1 compute
+// dP = dO V^T, dS = P (dP - D) with P handed over through LDS, and
+// dK^T += Q^T dS (V in registers).  The S waves run one pair ahead: in
+// step n they compute P of pair n+1 and dV of pair n while the dP waves
+// finish pair n, so each step has one barrier.  Q, lse (S waves) and dO, D
+// (dP waves) of pair n+3 are copied straight from memory into LDS slot
+// (n+3)%4 during step n; P rotates over two buffers.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dsum,
+    const bf16 *__restrict__ dout, const float *__restrict__ l2g, const float *__restrict__ dsum,
     bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int Hq, int Hkv, int W, int BG) {
-    constexpr int NT = NW * 64;
     __shared__ __align__(16) KvSmem<D, NW> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool role_s = wave < NW;                         // S/P/dV wave, else dP/dS/dK
+    const int slot = role_s ? wave : wave - NW;
     const int lq = lane & 31, hl = lane >> 5;
     const int bg = blockIdx.x % BG;
     const int kblk = blockIdx.x / BG;                      // earliest keys (most queries) first
@@ -311,130 +319,211 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const float scale = 1.0f / sqrtf((float)D);
     const int nQT = (S + kTile - 1) / kTile;
 
-    const int kt = kblk * NW + wave;                       // this wave's key tile
+    const int kt = kblk * NW + slot;                       // this wave's key tile
     const int j0 = kt * kTile;
     const bool wave_ok = j0 < S;
     const int qt_lo = kblk * NW;
     const int last_key = min(S - 1, (kblk * NW + NW) * kTile - 1);
     const int qt_hi = (int)min((long)nQT - 1, ((long)last_key + W - 1) / kTile);
 
-    // K and V rows of this wave's tile into its own LDS rows (B operands of S
-    // and dP: lane = key, dims 16ks + 8hl), read back every query tile.
+    // K (S waves) or V (dP waves) of this tile as B operands: lane = key,
+    // dims 16ks + 8hl.  Keys past the end read as zero; their columns are
+    // never stored.
+    bf16x8 kvf[D / 16];
     {
         const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTile, S - j0)));
         const uint32_t rs = (uint32_t)Hkv * D * 2;
         const size_t base = (((size_t)b * S + min(j0, S - 1)) * Hkv + g) * D;
-        const rsrc_t kr = make_rsrc(k + base, (uint32_t)rows * rs);
-        const rsrc_t vr = make_rsrc(v + base, (uint32_t)rows * rs);
-        constexpr int CH = D / 8;
+        const rsrc_t r = make_rsrc((role_s ? k : v) + base, (uint32_t)rows * rs);
 #pragma unroll
-        for (int u = 0; u < kTile * CH / 64; ++u) {
-            const int item = lane + 64 * u, row = item / CH, ch = item % CH;
-            *(bf16x8 *)&sm.kw[wave][row][8 * ch] = buf_load16(kr, row * rs + 16 * ch, 0);
-            *(bf16x8 *)&sm.vw[wave][row][8 * ch] = buf_load16(vr, row * rs + 16 * ch, 0);
-        }
+        for (int ks = 0; ks < D / 16; ++ks)
+            kvf[ks] = buf_load16(r, lq * rs + 2 * (16 * ks + 8 * hl), 0);
     }
-    const int frag_off = (int)(((const char *)&sm.kw[wave][lq][8 * hl]) - (const char *)&sm);
-    f32x16 dka[D / 32], dva[D / 32];
+    f32x16 acc[D / 32];                                    // dV^T (S waves) or dK^T
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-        dka[dt] = zero16();
-        dva[dt] = zero16();
-    }
-    // Flat pipeline over (head, query tile) pairs n: while pair n computes
-    // from buffer n&1, pair n+1 is in the other buffer and pair n+2 is in
-    // flight in registers.  One barrier per pair.
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+
+    // Pairs n = (head n / NQ, query tile qt_lo + n % NQ), walked with counters.
     const int NQ = qt_hi - qt_lo + 1, N = G * NQ;
-    KvStager<D, NT> st;
-    auto stage_load = [&](int n) {
-        st.load(q, dout, lse, dsum, b, g * G + n / NQ, (qt_lo + n % NQ) * kTile, S, Hq, tid);
+    // Do this tile's keys see any row of query tile qt?  (uniform)
+    auto active = [&](int qt) { return wave_ok && qt >= kt && (qt - kt) * kTile < W + kTile - 1; };
+    // x = A(pair in buffer bi) . kvf^T: S (S waves) or dP (dP waves), lane = key.
+    const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
+    auto scores = [&](int bi) {
+        const bf16 *arow = role_s ? sm.q[bi][arow_r] : sm.g[bi][arow_r];
+        f32x16 x = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            x = mfma32(*(const bf16x8 *)(arow + 8 * ((2 * ks + hl) ^ arow_s)), kvf[ks], x);
+        return x;
     };
-    stage_load(0);
-    st.store(sm, 0, tid);
-    if (N > 1) {
-        stage_load(1);
-        st.store(sm, 1, tid);
+    // P of a pair with query tile qt (S waves): masked, exponentiated, written to px[pb].
+    auto softmax = [&](f32x16 &x, int qt, int pbuf, int bi) {
+        const int r0 = qt * kTile;
+        // rows i = r0 + perm_row(r, hl), key j = j0 + lq: visible iff j <= i < j + W
+        const bool masked = qt == kt || (qt * kTile + kTile - 1) - W >= j0;
+        f32x4 *px = sm.px[pbuf][slot][0] + lane;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
+            const f32x4 l2v = *(const f32x4 *)&sm.l2[bi][row];
+            f32x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * u + e;
+                float y = x[r];
+                if (masked) {
+                    const int dij = (r0 + perm_row(r, hl)) - (j0 + lq);
+                    y = (dij >= 0 && dij < W) ? y : -INFINITY;
+                }
+                x[r] = __builtin_amdgcn_exp2f(fmaf(y, c, -l2v[e]));
+                pv[e] = x[r];
+            }
+            px[64 * u] = pv;
+        }
+    };
+    // acc += A^T(buffer bi) . (xa, xb): dV^T (S waves, dO^T) or dK^T (dP waves,
+    // Q^T).  A row m = dim 32dt + m, k = query 16kk + 8hl + 0..7, read from the
+    // row tile with two transposing reads of 4 queries each.
+    const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+    auto accumulate = [&](const bf16x8 &xa, const bf16x8 &xb, int bi) {
+        const bf16(*t)[D] = role_s ? sm.g[bi] : sm.q[bi];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d = 32 * dt + tr_d, c = d >> 3, half = (d >> 2) & 1;
+            bf16x8 a[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
+                const bf16x4 lo = lds_read_tr(&t[r1][8 * (c ^ swz<D>(r1)) + 4 * half]);
+                const bf16x4 hi = lds_read_tr(&t[r2][8 * (c ^ swz<D>(r2)) + 4 * half]);
+                a[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            acc[dt] = mfma32(a[0], xa, acc[dt]);
+            acc[dt] = mfma32(a[1], xb, acc[dt]);
+        }
+    };
+
+    // Staging by DMA: S waves copy Q rows and lse*log2(e), dP waves dO rows
+    // and D, of the pairs in order; IPW instructions of 1 KB per wave and
+    // tile (wave 0 of each role also copies the 128-byte row vector).
+    constexpr int CPR = D / 8;                             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                          // rows per DMA instruction
+    constexpr int IPW = kTile / RPI / NW;                  // instructions per wave and tile
+    static_assert(IPW >= 1 && IPW * NW * RPI == kTile, "DMA split");
+    const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
+    const bf16 *tsrc = role_s ? q : dout;
+    const float *vsrc = role_s ? l2g : dsum;
+    uint32_t dma_off[IPW];                                 // row * row_bytes + swizzled chunk
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+        const int row = (slot * IPW + u) * RPI + lane / CPR;
+        dma_off[u] = row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row));
     }
-    if (N > 2) stage_load(2);
+    int ld_h = g * G, ld_t = 0;                            // next pair to copy
+    auto stage = [&](int sl) {
+        const int r0 = (qt_lo + ld_t) * kTile;
+        const int rows = min(kTile, S - r0);
+        const size_t base = (((size_t)b * S + r0) * Hq + ld_h) * D;
+        const u32x4 r = sgpr_rsrc(tsrc + base, (uint32_t)(rows - 1) * qrow_bytes + D * 2);
+        bf16(*tile)[D] = role_s ? sm.q[sl] : sm.g[sl];
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) dma16(r, tile[(slot * IPW + u) * RPI], dma_off[u]);
+        if (slot == 0) {
+            const u32x4 rv = sgpr_rsrc(vsrc + ((size_t)b * Hq + ld_h) * S + r0, (uint32_t)rows * 4);
+            if (lane < kTile / 4) dma16(rv, role_s ? sm.l2[sl] : sm.dd[sl], 16 * lane);
+        }
+        if (++ld_t == NQ) {
+            ld_t = 0;
+            ++ld_h;
+        }
+    };
+    // Wait for this wave's copies except those of the current step (newer).
+    auto dma_wait = [&](bool newer) {
+        if (!newer) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (slot == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+    };
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) retire(kvf[ks]);
+    for (int n = 0; n < 3 && n < N; ++n) stage(n);
+    dma_wait(false);
     lds_barrier();
 
-    for (int n = 0; n < N; ++n) {
-        const int buf = n & 1;
-        const int qt = qt_lo + n % NQ;
-        const int r0 = qt * kTile;
-        // Does this wave's key tile see any row of the query tile?
-        const bool active = wave_ok && qt >= kt && (qt - kt) * kTile < W + kTile - 1;
-        if (active) {                                      // wave-uniform
-            // Re-read K/V fragments from LDS every pair (an opaque offset keeps
-            // the compiler from hoisting 64 registers' worth of them).
-            int fo = frag_off;
-            asm volatile("" : "+v"(fo));
-            const bf16 *kfrag = (const bf16 *)((const char *)&sm + fo);
-            const bf16 *vfrag = kfrag + (sizeof(sm.kw) / sizeof(bf16));
-            const bf16 *qrow = &sm.q[buf][score_row_key(lq)][8 * hl];
-            const bf16 *grow = &sm.g[buf][score_row_key(lq)][8 * hl];
-            f32x16 s = mfma32(*(const bf16x8 *)qrow, *(const bf16x8 *)kfrag, zero16());
-            f32x16 dp = mfma32(*(const bf16x8 *)grow, *(const bf16x8 *)vfrag, zero16());
-#pragma unroll
-            for (int ks = 1; ks < D / 16; ++ks) {
-                s = mfma32(*(const bf16x8 *)(qrow + 16 * ks), *(const bf16x8 *)(kfrag + 16 * ks), s);
-                dp = mfma32(*(const bf16x8 *)(grow + 16 * ks), *(const bf16x8 *)(vfrag + 16 * ks), dp);
+    bf16x8 pa, pb;                                         // P of pair n (S waves)
+    if (role_s && active(qt_lo)) {
+        f32x16 x = scores(0);
+        softmax(x, qt_lo, 0, 0);
+        pa = pack8(x, 0);
+        pb = pack8(x, 1);
+    }
+    lds_barrier();
+
+    // Step n (one barrier each): copy pair n+3 into slot (n+3)%4; S waves:
+    // P of pair n+1, dV of pair n; dP waves: dS and dK of pair n; then wait
+    // for pair n+2's copy (issued in step n-1) before the barrier.
+    int t_cur = 0;                                         // query tile index of pair n
+    if (role_s) {
+        for (int n = 0; n < N; ++n) {
+            const int bi = n % kKvSlots, bn = (n + 1) % kKvSlots;
+            const int t_next = t_cur + 1 == NQ ? 0 : t_cur + 1;
+            const int qt = qt_lo + t_cur, qn = qt_lo + t_next;
+            const bool copy = n + 3 < N;
+            if (copy) stage((n + 3) % kKvSlots);
+            bf16x8 na, nb;
+            const bool next = n + 1 < N && active(qn);
+            if (next) {
+                f32x16 x = scores(bn);
+                softmax(x, qn, (n + 1) & 1, bn);
+                na = pack8(x, 0);
+                nb = pack8(x, 1);
             }
-            // rows i = r0 + perm_row(r, hl), key j = j0 + lq: visible iff j <= i < j + W
-            const bool masked = qt == kt || (qt * kTile + kTile - 1) - W >= j0;
-            f32x16 &p = s, &ds = dp;                       // computed in place
-            {
-                f32x4 l2v[4], ddv[4];
+            if (active(qt)) accumulate(pa, pb, bi);
+            if (next) {
+                pa = na;
+                pb = nb;
+            }
+            dma_wait(copy);
+            lds_barrier();                                 // step n done: slot n%4, px[n&1] free
+            t_cur = t_next;
+        }
+    } else {
+        for (int n = 0; n < N; ++n) {
+            const int bi = n % kKvSlots;
+            const int qt = qt_lo + t_cur;
+            const bool copy = n + 3 < N;
+            if (copy) stage((n + 3) % kKvSlots);
+            if (active(qt)) {
+                f32x16 x = scores(bi);
+                const f32x4 *px = sm.px[n & 1][slot][0] + lane;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
-                    l2v[u] = *(const f32x4 *)&sm.l2[buf][row];
-                    ddv[u] = *(const f32x4 *)&sm.dd[buf][row];
-                }
+                    const f32x4 ddv = *(const f32x4 *)&sm.dd[bi][row];
+                    const f32x4 pv = px[64 * u];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[r];
-                    if (masked) {
-                        const int dij = (r0 + perm_row(r, hl)) - (j0 + lq);
-                        x = (dij >= 0 && dij < W) ? x : -INFINITY;
-                    }
-                    const float l2r = l2v[r >> 2][r & 3], ddr = ddv[r >> 2][r & 3];
-                    const float pr = __builtin_amdgcn_exp2f(fmaf(x, c, -l2r));
-                    ds[r] = pr * (dp[r] - ddr);
-                    p[r] = pr;
+                    for (int e = 0; e < 4; ++e) x[4 * u + e] = pv[e] * (x[4 * u + e] - ddv[e]);
                 }
+                accumulate(pack8(x, 0), pack8(x, 1), bi);
             }
-            const bf16x8 pa = pack8(p, 0), pb = pack8(p, 1);
-            const bf16x8 da = pack8(ds, 0), db = pack8(ds, 1);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                dva[dt] = mfma32(*(const bf16x8 *)&sm.gt[buf][32 * dt + lq][8 * hl], pa, dva[dt]);
-                dva[dt] = mfma32(*(const bf16x8 *)&sm.gt[buf][32 * dt + lq][16 + 8 * hl], pb, dva[dt]);
-                dka[dt] = mfma32(*(const bf16x8 *)&sm.qt[buf][32 * dt + lq][8 * hl], da, dka[dt]);
-                dka[dt] = mfma32(*(const bf16x8 *)&sm.qt[buf][32 * dt + lq][16 + 8 * hl], db, dka[dt]);
-            }
-        }
-        lds_barrier();                                     // buffer n&1 released
-        if (n + 2 < N) {
-            st.store(sm, buf, tid);                        // pair n+2 into the freed buffer
-            if (n + 3 < N) stage_load(n + 3);
+            dma_wait(copy);
+            lds_barrier();                                 // step n done
+            t_cur = t_cur + 1 == NQ ? 0 : t_cur + 1;
         }
     }
 
     if (wave_ok && j0 + lq < S) {
         const size_t off = (((size_t)b * S + j0 + lq) * Hkv + g) * D;
+        bf16 *dst = role_s ? dv : dk;
+        const float f = role_s ? 1.0f : scale;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                bf16x4 xk, xv;
+                bf16x4 xo;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xk[e] = (bf16)(dka[dt][4 * jj + e] * scale);
-                    xv[e] = (bf16)dva[dt][4 * jj + e];
-                }
-                *(bf16x4 *)(dk + off + 32 * dt + 8 * jj + 4 * hl) = xk;
-                *(bf16x4 *)(dv + off + 32 * dt + 8 * jj + 4 * hl) = xv;
+                for (int e = 0; e < 4; ++e) xo[e] = (bf16)(acc[dt][4 * jj + e] * f);
+                *(bf16x4 *)(dst + off + 32 * dt + 8 * jj + 4 * hl) = xo;
             }
     }
 }
@@ -450,7 +539,7 @@ hipError_t launch_dq(const BackwardArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-constexpr int kKvWaves = 4;        // key tiles per dk/dv work-group
+constexpr int kKvWaves = 4;        // key tiles per dk/dv work-group (two waves each)
 
 template <int D>
 hipError_t launch_dkdv(const BackwardArgs &a, hipStream_t stream) {
@@ -458,8 +547,8 @@ hipError_t launch_dkdv(const BackwardArgs &a, hipStream_t stream) {
     const int nKT = (a.S + kTile - 1) / kTile;
     const int nblk = (nKT + kKvWaves - 1) / kKvWaves;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kKvWaves>), dim3((unsigned)((long)BG * nblk)),
-                       dim3(kKvWaves * 64), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                       (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.ws_dsum, (bf16 *)a.dk,
+                       dim3(2 * kKvWaves * 64), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                       (const bf16 *)a.v, (const bf16 *)a.dout, a.ws_l2, a.ws_dsum, (bf16 *)a.dk,
                        (bf16 *)a.dv, a.S, a.Hq, a.Hkv, a.window, BG);
     return hipGetLastError();
 }

@@ -57,6 +57,7 @@ struct BackwardArgs {
     void *dq, *dk, *dv;
     float *dsink;
     float *ws_dsum;             // [B, Hq, S]: D_i = dO_i . O_i
+    float *ws_l2;               // [B, Hq, S]: lse_i * log2(e)
     float *ws_part;             // [B, Hq, ceil(S/32)]: sink-gradient partials
     int B, Hq, Hkv, S, D, window;
 };

@@ -178,7 +178,7 @@ def test_backward_rejects(lib, kw, code):
 
 def test_backward_workspace_and_empty(lib):
     # D_i per (b, h, row) plus one sink-gradient partial per 32 rows, float32
-    assert lib.swa_sink_backward_workspace_bytes(2, 64, 1000) == 4 * 2 * 64 * (1000 + 32)
+    assert lib.swa_sink_backward_workspace_bytes(2, 64, 1000) == 4 * 2 * 64 * (2 * 1000 + 32)
     assert lib.swa_sink_backward_workspace_bytes(0, 64, 1000) == 0
     assert bwd(lib, B=0, ws=None, wsb=0) == _lib.SWA_OK
     assert bwd(lib, S=0, ws=None, wsb=0) == _lib.SWA_OK
