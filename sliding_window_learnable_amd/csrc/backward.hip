@@ -231,6 +231,13 @@ hipError_t launch_backward_pre(const BackwardArgs &a, hipStream_t stream, bool b
     return bf16_inputs ? launch_pre<bf16>(a, stream) : launch_pre<float>(a, stream);
 }
 
+hipError_t launch_backward_dsink(const BackwardArgs &a, hipStream_t stream) {
+    const int tiles = (a.S + kRows - 1) / kRows;
+    hipLaunchKernelGGL(dsink_kernel, dim3(a.Hq), dim3(64), 0, stream, a.ws_part, a.dsink, a.B,
+                       a.Hq, tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_backward_bf16_rowwise(const BackwardArgs &a, hipStream_t stream) {
     return launch_generic<bf16>(a, stream);
 }

@@ -35,201 +35,11 @@ constexpr int kTile = 32;
 // Row of the permuted accumulator layout: register r of lane half hl.
 __device__ __forceinline__ int perm_row(int r, int hl) { return 16 * (r >> 3) + 8 * hl + (r & 7); }
 
-// 4 rows x 8 dims quad written transposed: dst[8ch + e][col..col+3].
-template <int LD>
-__device__ __forceinline__ void store_transposed(bf16 (*dst)[LD], const bf16x8 (&quad)[4], int ch,
-                                                 int col) {
-    u32x2 w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bf16x4 x;
-        x[0] = quad[0][e];
-        x[1] = quad[1][e];
-        x[2] = quad[2][e];
-        x[3] = quad[3][e];
-        w[e] = __builtin_bit_cast(u32x2, x);
-        *(u32x2 *)&dst[8 * ch + e][col] = w[e];
-    }
-    lds_settle(w);
-}
-
-// =========================================================================== dq
-
-template <int D>
-struct DqSmem {
-    bf16 k[2][kTile][D + 8];
-    bf16 v[2][kTile][D + 8];
-    bf16 kt[2][D][kTile + 8];
-};
-
-// One 32-key tile: K and V as 4-row x 8-dim quads (rows past the end read
-// zeros); K rows, V rows and K^T are written to a slot.
-template <int D, int NT>
-struct DqLoader {
-    static constexpr int CH = D / 8;
-    static constexpr int QPT = (2 * 8 * CH + NT - 1) / NT;   // K and V quads per thread
-    bf16x8 quad[QPT][4];
-
-    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, size_t row_elems,
-                                         uint32_t rs, int S, int T, int tid) {
-        const int rows = min(kTile, S - kTile * T);
-        const uint32_t bytes = rows > 0 ? (uint32_t)rows * rs : 0u;
-        const rsrc_t kr = make_rsrc(kb + (size_t)kTile * T * row_elems, bytes);
-        const rsrc_t vr = make_rsrc(vb + (size_t)kTile * T * row_elems, bytes);
-#pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < 2 * 8 * CH) {                        // wave-uniform (multiples of 64)
-                const int it = item % (8 * CH), kq = it & 7, ch = it >> 3;
-                // K or V: the same for the whole wave (64-aligned item ranges),
-                // stated so that the descriptor stays scalar.
-                const bool is_k = __builtin_amdgcn_readfirstlane(item / (8 * CH)) == 0;
-                const rsrc_t r = is_k ? kr : vr;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) quad[i][j] = buf_load16(r, (4 * kq + j) * rs + 16 * ch, 0);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(DqSmem<D> &sm, int slot, int tid) const {
-#pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < 2 * 8 * CH) {
-                const bool is_k = __builtin_amdgcn_readfirstlane(item / (8 * CH)) == 0;
-                const int it = item % (8 * CH), kq = it & 7, ch = it >> 3;
-                bf16(*rows)[D + 8] = is_k ? sm.k[slot] : sm.v[slot];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) *(bf16x8 *)&rows[4 * kq + j][8 * ch] = quad[i][j];
-                lds_settle(quad[i]);
-                if (is_k) store_transposed(sm.kt[slot], quad[i], ch, 4 * kq);
-            }
-        }
-    }
-};
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dsum,
-    bf16 *__restrict__ dq, int S, int Hq, int Hkv, int W, int BG, int NB) {
-    constexpr int NT = NW * 64;
-    __shared__ __align__(16) DqSmem<D> sm;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lq = lane & 31, hl = lane >> 5;
-    const int bg = blockIdx.x % BG;
-    const int qb = NB - 1 - blockIdx.x / BG;              // longest query blocks first
-    const int b = bg / Hkv, g = bg % Hkv;
-    const int G = Hq / Hkv;
-    const float c = kLog2e / sqrtf((float)D);
-    const float scale = 1.0f / sqrtf((float)D);
-
-    const int i0 = qb * kTile;
-    const int p_first = i0, p_last = min(S - 1, i0 + kTile - 1);
-    const int T_lo = max(0, p_first - W + 1) / kTile;
-    const int T_hi = p_last / kTile;
-    const int n_tiles = T_hi - T_lo + 1;
-
-    const size_t row_elems = (size_t)Hkv * D;
-    const uint32_t rs = (uint32_t)row_elems * 2;
-    const bf16 *kb = k + ((size_t)b * S * Hkv + g) * D;
-    const bf16 *vb = v + ((size_t)b * S * Hkv + g) * D;
-
-    const int i = i0 + lq;
-    const bool row_ok = i < S;
-    const int pq = min(i, S - 1);
-    const int kbias = 8 * hl - pq;                         // key - query = 32T + 16(r>>3) + (r&7) + kbias
-    auto tile_masked = [&](int T) {
-        return kTile * T + kTile - 1 > p_first || kTile * T <= p_last - W;
-    };
-
-    DqLoader<D, NT> ld;
-    for (int hh = wave; hh < G; hh += NW) {
-        const int h = g * G + hh;
-        if (hh != wave) lds_barrier();
-        ld.load(kb, vb, row_elems, rs, S, T_lo, tid);
-        ld.store(sm, 0, tid);
-        lds_barrier();
-
-        bf16x8 qf[D / 16], gf[D / 16];
-        {
-            const size_t off = (((size_t)b * S + pq) * Hq + h) * D + 8 * hl;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                qf[ks] = *(const bf16x8 *)(q + off + 16 * ks);
-                gf[ks] = *(const bf16x8 *)(dout + off + 16 * ks);
-            }
-        }
-        const size_t li = ((size_t)b * Hq + h) * S + pq;
-        const float l2 = lse[li] * kLog2e;
-        const float Di = dsum[li];
-        f32x16 acc[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            retire(qf[ks]);
-            retire(gf[ks]);
-        }
-
-        for (int t = 0; t < n_tiles; ++t) {
-            const int T = T_lo + t, slot = t & 1;
-            if (t + 1 < n_tiles) ld.load(kb, vb, row_elems, rs, S, T + 1, tid);
-            const bf16 *krow = &sm.k[slot][score_row_key(lq)][8 * hl];
-            const bf16 *vrow = &sm.v[slot][score_row_key(lq)][8 * hl];
-            f32x16 st = mfma32(*(const bf16x8 *)krow, qf[0], zero16());
-            f32x16 dpt = mfma32(*(const bf16x8 *)vrow, gf[0], zero16());
-#pragma unroll
-            for (int ks = 1; ks < D / 16; ++ks) {
-                st = mfma32(*(const bf16x8 *)(krow + 16 * ks), qf[ks], st);
-                dpt = mfma32(*(const bf16x8 *)(vrow + 16 * ks), gf[ks], dpt);
-            }
-            if (tile_masked(T)) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int dk = kTile * T + 16 * (r >> 3) + (r & 7) + kbias;
-                    st[r] = (dk <= 0 && dk > -W) ? st[r] : -INFINITY;
-                }
-            }
-            f32x16 ds;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(st[r], c, -l2));
-                ds[r] = p * (dpt[r] - Di);
-            }
-            const bf16x8 da = pack8(ds, 0), db = pack8(ds, 1);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                acc[dt] = mfma32(*(const bf16x8 *)&sm.kt[slot][32 * dt + lq][8 * hl], da, acc[dt]);
-                acc[dt] = mfma32(*(const bf16x8 *)&sm.kt[slot][32 * dt + lq][16 + 8 * hl], db, acc[dt]);
-            }
-            if (t + 1 < n_tiles) ld.store(sm, (t + 1) & 1, tid);
-            lds_barrier();
-        }
-
-        if (row_ok) {
-            bf16 *orow = dq + (((size_t)b * S + i) * Hq + h) * D;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    bf16x4 x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[dt][4 * jj + e] * scale);
-                    *(bf16x4 *)(orow + 32 * dt + 8 * jj + 4 * hl) = x;
-                }
-        }
-    }
-}
-
-// ========================================================================= dk/dv
-
-// Q and dO tiles are unpadded rows whose 16-byte chunks are XOR-swizzled by
-// row (chunk c of row r sits at c ^ swz(r)), so that both the row reads of
-// S and dP (16 rows, one chunk) and the transposing reads of dK and dV
-// (4 rows x 32 dims per 32 lanes) hit distinct banks.
+// Operand tiles (Q, dO, K, V) are unpadded rows whose 16-byte chunks are
+// XOR-swizzled by row (chunk c of row r sits at c ^ swz(r)), so that both
+// the row reads of score products (16 rows, one chunk) and the transposing
+// reads of gradient products (4 rows x 32 dims per 32 lanes) hit distinct
+// banks.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -274,6 +84,201 @@ __device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// =========================================================================== dq
+
+constexpr int kDqSlots = 4;     // key tiles t, t+1, t+2 landed or landing, t+3 in flight
+
+template <int D>
+struct DqSmem {
+    bf16 k[kDqSlots][kTile][D];     // K rows (swizzled): A of S^T = K Q^T, read transposed for dQ
+    bf16 v[kDqSlots][kTile][D];     // V rows (swizzled): A of dP^T = V dO^T
+};
+
+// One work-group per (batch, KV head, 32 query rows), one wave per query
+// head (NW at a time).  Before the key loop a wave also computes, for its
+// rows, D_i = dO_i . O_i and lse_i log2(e) (written to the workspace for
+// the dk/dv kernel) and the row tile's sink-gradient partial.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ out, const bf16 *__restrict__ dout, const float *__restrict__ lse,
+    const float *__restrict__ sink, float *__restrict__ dsum, float *__restrict__ l2g,
+    float *__restrict__ part, bf16 *__restrict__ dq, int S, int Hq, int Hkv, int W, int BG, int NB) {
+    __shared__ __align__(16) DqSmem<D> sm;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hl = lane >> 5;
+    const int bg = blockIdx.x % BG;
+    const int qb = NB - 1 - blockIdx.x / BG;              // longest query blocks first
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int G = Hq / Hkv;
+    const float c = kLog2e / sqrtf((float)D);
+    const float scale = 1.0f / sqrtf((float)D);
+
+    const int i0 = qb * kTile;
+    const int p_first = i0, p_last = min(S - 1, i0 + kTile - 1);
+    const int T_lo = max(0, p_first - W + 1) / kTile;
+    const int T_hi = p_last / kTile;
+    const int n_tiles = T_hi - T_lo + 1;
+
+    const uint32_t rs = (uint32_t)Hkv * D * 2;
+    const bf16 *kb = k + ((size_t)b * S * Hkv + g) * D;
+    const bf16 *vb = v + ((size_t)b * S * Hkv + g) * D;
+
+    const int i = i0 + lq;
+    const bool row_ok = i < S;
+    const int pq = min(i, S - 1);
+    const int kbias = 8 * hl - pq;                         // key - query = 32T + 16(r>>3) + (r&7) + kbias
+    auto tile_masked = [&](int T) {
+        return kTile * T + kTile - 1 > p_first || kTile * T <= p_last - W;
+    };
+
+    // K and V tiles by buffer->LDS copies: 2 * 32 * 2D bytes in 1 KB
+    // instructions, IPW per wave (K first, then V), chunks swizzled by row.
+    constexpr int CPR = D / 8;                             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                          // rows per instruction
+    constexpr int NI = 2 * kTile / RPI;                    // instructions per tile (K and V)
+    constexpr int IPW = NI / NW;
+    static_assert(IPW >= 1 && IPW * NW == NI, "DMA split");
+    uint32_t dma_off[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+        const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
+        dma_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
+    }
+    auto stage = [&](int T, int sl) {
+        const int rows = min(kTile, S - kTile * T);
+        const uint32_t bytes = (uint32_t)(rows - 1) * rs + D * 2;
+        const size_t off = (size_t)kTile * T * Hkv * D;
+        const u32x4 kr = sgpr_rsrc(kb + off, bytes), vr = sgpr_rsrc(vb + off, bytes);
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ii = wave * IPW + u;                 // uniform
+            const bool is_k = ii < NI / 2;
+            bf16(*tile)[D] = is_k ? sm.k[sl] : sm.v[sl];
+            dma16(is_k ? kr : vr, tile[(ii % (NI / 2)) * RPI], dma_off[u]);
+        }
+    };
+    auto dma_wait = [&](bool newer) {
+        if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
+    const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+
+    for (int hh = wave; hh < G; hh += NW) {
+        const int h = g * G + hh;
+        if (hh != wave) lds_barrier();                     // previous head's tiles released
+
+        bf16x8 qf[D / 16], gf[D / 16];
+        float dsum_part = 0.0f;
+        {
+            const size_t off = (((size_t)b * S + pq) * Hq + h) * D + 8 * hl;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                qf[ks] = *(const bf16x8 *)(q + off + 16 * ks);
+                gf[ks] = *(const bf16x8 *)(dout + off + 16 * ks);
+                const bf16x8 of = *(const bf16x8 *)(out + off + 16 * ks);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dsum_part = fmaf((float)gf[ks][e], (float)of[e], dsum_part);
+            }
+        }
+        const size_t li = ((size_t)b * Hq + h) * S + pq;
+        const float lse_i = lse[li];
+        const float l2 = lse_i * kLog2e;
+        const float Di = dsum_part + __shfl_xor(dsum_part, 32);
+        {
+            // D_i and lse log2(e) for the dk/dv kernel; this row tile's
+            // partial of the sink gradient, sum_i e^{s_h - lse_i} D_i.
+            if (row_ok && hl == 0) {
+                dsum[li] = Di;
+                l2g[li] = l2;
+            }
+            const float sh = sink[h];
+            float term = (row_ok && hl == 0 && sh != -INFINITY) ? expf(sh - lse_i) * Di : 0.0f;
+            for (int m = 1; m < 64; m <<= 1) term += __shfl_xor(term, m);
+            if (lane == 0) part[((size_t)b * Hq + h) * NB + qb] = term;
+        }
+        f32x16 acc[D / 32];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            retire(qf[ks]);
+            retire(gf[ks]);
+        }
+
+        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
+        dma_wait(false);
+        lds_barrier();
+
+        for (int t = 0; t < n_tiles; ++t) {
+            const int T = T_lo + t, sl = t % kDqSlots;
+            const bool copy = t + 3 < n_tiles;
+            if (copy) stage(T + 3, (t + 3) % kDqSlots);
+            const bf16 *krow = sm.k[sl][arow_r];
+            const bf16 *vrow = sm.v[sl][arow_r];
+            f32x16 st = zero16(), dpt = zero16();
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int ch = 8 * ((2 * ks + hl) ^ arow_s);
+                st = mfma32(*(const bf16x8 *)(krow + ch), qf[ks], st);
+                dpt = mfma32(*(const bf16x8 *)(vrow + ch), gf[ks], dpt);
+            }
+            if (tile_masked(T)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dk = kTile * T + 16 * (r >> 3) + (r & 7) + kbias;
+                    st[r] = (dk <= 0 && dk > -W) ? st[r] : -INFINITY;
+                }
+            }
+            f32x16 ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[r], c, -l2));
+                ds[r] = p * (dpt[r] - Di);
+            }
+            const bf16x8 da = pack8(ds, 0), db = pack8(ds, 1);
+            // dQ^T += K^T dS^T: A row m = dim 32dt + m, k = key 16kk + 8hl + 0..7,
+            // from the K row tile by transposing reads of 4 keys each.
+            const bf16(*kt)[D] = sm.k[sl];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int d = 32 * dt + tr_d, cc = d >> 3, half = (d >> 2) & 1;
+                bf16x8 a[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
+                    const bf16x4 lo = lds_read_tr(&kt[r1][8 * (cc ^ swz<D>(r1)) + 4 * half]);
+                    const bf16x4 hi = lds_read_tr(&kt[r2][8 * (cc ^ swz<D>(r2)) + 4 * half]);
+                    a[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                acc[dt] = mfma32(a[0], da, acc[dt]);
+                acc[dt] = mfma32(a[1], db, acc[dt]);
+            }
+            dma_wait(copy);
+            lds_barrier();                                 // tile t's slot released
+        }
+
+        if (row_ok) {
+            bf16 *orow = dq + (((size_t)b * S + i) * Hq + h) * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[dt][4 * jj + e] * scale);
+                    *(bf16x4 *)(orow + 32 * dt + 8 * jj + 4 * hl) = x;
+                }
+        }
+    }
+}
+
+// ========================================================================= dk/dv
 
 constexpr int kKvSlots = 4;     // staging slots: pairs n, n+1 in use, n+2 landed, n+3 in flight
 
@@ -534,8 +539,8 @@ hipError_t launch_dq(const BackwardArgs &a, hipStream_t stream) {
     const int NB = (a.S + kTile - 1) / kTile;
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)((long)BG * NB)), dim3(NW * 64), 0,
                        stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                       (const bf16 *)a.dout, a.lse, a.ws_dsum, (bf16 *)a.dq, a.S, a.Hq, a.Hkv,
-                       a.window, BG, NB);
+                       (const bf16 *)a.out, (const bf16 *)a.dout, a.lse, a.sink, a.ws_dsum, a.ws_l2,
+                       a.ws_part, (bf16 *)a.dq, a.S, a.Hq, a.Hkv, a.window, BG, NB);
     return hipGetLastError();
 }
 
@@ -563,14 +568,16 @@ hipError_t launch_d(const BackwardArgs &a, hipStream_t stream) {
     default: e = launch_dq<D, 1>(a, stream); break;
     }
     if (e != hipSuccess) return e;
+    e = launch_backward_dsink(a, stream);
+    if (e != hipSuccess) return e;
     return launch_dkdv<D>(a, stream);
 }
 
 }  // namespace
 
+// dq (with D_i, lse log2(e) and the sink-gradient partials), the sink
+// gradient, then dk/dv (which reads D_i and lse log2(e)).
 hipError_t launch_backward_bf16(const BackwardArgs &a, hipStream_t stream) {
-    hipError_t e = launch_backward_pre(a, stream, true);
-    if (e != hipSuccess) return e;
     return a.D == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
 }
 

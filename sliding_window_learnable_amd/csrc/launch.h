@@ -63,6 +63,8 @@ struct BackwardArgs {
 };
 size_t backward_workspace_bytes(int B, int Hq, int S);
 hipError_t launch_backward_pre(const BackwardArgs &a, hipStream_t stream, bool bf16_inputs);
+// dsink_h = -(sum of the per-32-row partials in ws_part), fixed order.
+hipError_t launch_backward_dsink(const BackwardArgs &a, hipStream_t stream);
 hipError_t launch_backward_f32(const BackwardArgs &a, hipStream_t stream);
 hipError_t launch_backward_bf16(const BackwardArgs &a, hipStream_t stream);
 // one wave per output row, bf16 in/out (reference-structured; not dispatched)
