@@ -11,6 +11,8 @@ same JSON object:
   decode        ring-cache decode, B=256, 128 slots, T_q = 1 and 4, in HBM GB/s
   hybrid_5to1   5 SWA layers + 1 global layer at S=65536: per-layer-type time
   long_context  SWA prefill at S=262144; global decode B=8 over 262144 keys
+  backward      swa_sink_backward (dq, dk, dv, dsink) at the 32K SWA workload
+                and on a 16K global layer, with the forward time beside it
 Inputs are seeded synthetic Gaussian tensors resident in HBM before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTION]
@@ -46,7 +48,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "decode", "hybrid", "long", "copy"])
+                    choices=["all", "prefill", "decode", "hybrid", "long", "backward", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -260,6 +262,44 @@ def bench_long(args, swa, acc, torch):
     return res
 
 
+def bench_backward(args, swa, acc, torch):
+    """swa_sink_backward (dq, dk, dv, dsink; bf16) on the 32K SWA prefill
+    workload and on a 16K global causal layer, against the forward call."""
+    from sliding_window_learnable_amd import inputs
+    res = {"workload": "swa_sink_backward bf16, B=1 Hq=64 Hkv=8 D=128: window 128 at S=32768 "
+                       "and global causal (window = S) at S=16384",
+           "flop_rule": "10 D per attended (row, head, key): q.k and dO.v recomputed, dq, dk, dv"}
+    B, Hq, Hkv, D = 1, 64, 8, 128
+    for name, S, W, steps in (("swa_32768", 32768, 128, 40), ("global_16384", 16384, 16384, 6)):
+        q, k, v, sink = inputs.attention_inputs(2, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+        g = inputs.upstream_grad(2, 0, B, S, Hq, D, torch.bfloat16, "cuda")
+        out = torch.empty_like(q)
+        lse = torch.empty((B, Hq, S), device="cuda", dtype=torch.float32)
+        if W < S:
+            fwd = lambda i: swa.swa_sink_prefill(q, k, v, sink, W, out=out, lse=lse)
+        else:
+            fwd = lambda i: swa.global_sink_attn(q, k, v, sink, out=out, lse=lse)
+        fwd(0)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsink = torch.empty_like(sink)
+        ws = torch.empty(swa.swa_sink_backward_workspace_bytes(B, Hq, S), device="cuda",
+                         dtype=torch.uint8)
+        log("backward %s: %d steps" % (name, steps))
+        ms_b = timed(lambda i: swa.swa_sink_backward(q, k, v, sink, out, lse, g, W, dq=dq, dk=dk,
+                                                     dv=dv, dsink=dsink, workspace=ws),
+                     steps, max(2, steps // 4))
+        ms_f = timed(fwd, steps, max(2, steps // 4))
+        fl = acc.backward_flops(B, S, Hq, D, min(W, S))
+        nb = acc.backward_bytes(B, S, Hq, Hkv, D)
+        res[name] = dict(ms=ms_b, tflops=fl / (ms_b * 1e-3) / 1e12,
+                         frac_mfma_peak=fl / (ms_b * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
+                         hbm_gbs=nb / (ms_b * 1e-3) / 1e9, forward_ms=ms_f,
+                         backward_over_forward=ms_b / ms_f, tokens_per_s=B * S / (ms_b * 1e-3))
+        del q, k, v, sink, g, out, lse, dq, dk, dv, dsink, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy(args, torch):
     """Plain 1 GiB device copy: the reference kernel for scaling PMC byte counters."""
     n = 1 << 30
@@ -330,6 +370,8 @@ def main():
         result["hybrid_5to1"] = bench_hybrid(args, swa, acc, torch)
     if args.only in ("all", "long"):
         result["long_context"] = bench_long(args, swa, acc, torch)
+    if args.only in ("all", "backward"):
+        result["backward"] = bench_backward(args, swa, acc, torch)
     print(json.dumps(result))
 
 

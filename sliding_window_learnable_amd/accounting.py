@@ -62,6 +62,19 @@ def global_bytes(B, S_q, S_kv, Hq, Hkv, D, elt=BF16, with_lse=True) -> int:
     return qo + kv + (B * Hq * S_q * F32 if with_lse else 0)
 
 
+def backward_flops(B, S, Hq, D, W) -> int:
+    """Attention backward: 10 * D per attended (row, head, key) pair -- the
+    recomputed q.k (2D) and dO.v (2D), and dv, dk, dq (2D each)."""
+    return 10 * D * Hq * B * window_pairs(S, W)
+
+
+def backward_bytes(B, S, Hq, Hkv, D, elt=BF16) -> int:
+    """q, k, v, out, dout, lse read once; dq, dk, dv written once."""
+    q_like = 4 * B * S * Hq * D * elt          # q, out, dout read; dq written
+    kv_like = 4 * B * S * Hkv * D * elt        # k, v read; dk, dv written
+    return q_like + kv_like + B * Hq * S * F32
+
+
 def decode_flops(B, T, Hq, D, W, L=None) -> int:
     L = W if L is None else L
     return 4 * D * Hq * B * ring_pairs(T, W, L)
