@@ -35,55 +35,6 @@ constexpr int kTile = 32;
 // Row of the permuted accumulator layout: register r of lane half hl.
 __device__ __forceinline__ int perm_row(int r, int hl) { return 16 * (r >> 3) + 8 * hl + (r & 7); }
 
-// Operand tiles (Q, dO, K, V) are unpadded rows whose 16-byte chunks are
-// XOR-swizzled by row (chunk c of row r sits at c ^ swz(r)), so that both
-// the row reads of score products (16 rows, one chunk) and the transposing
-// reads of gradient products (4 rows x 32 dims per 32 lanes) hit distinct
-// banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16: in each 16-lane group, lane j supplies the address of
-// 4 bf16 (row j/4, dims 4(j%4)..+3 of a 16-dim span); lane i receives the
-// element at dim i of each of the 4 rows.
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
-    return __builtin_bit_cast(bf16x4, r);
-}
-
-// Buffer descriptor as four scalar dwords (raw buffer, num_records bytes).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
-    const unsigned long long p = (unsigned long long)base;
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
-    r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
-    r[2] = __builtin_amdgcn_readfirstlane(bytes);
-    r[3] = 0x00020000u;
-    return r;
-}
-
-// Buffer -> LDS copy (no registers): lane l's 16 bytes at voff land at
-// lds + 16 l; out-of-range dwords land as zero.  Written as asm so that the
-// compiler does not wait for every copy before each LDS read (it cannot
-// tell the copies' targets from the tiles being read); the copies are
-// waited for explicitly (vmcnt) before the barrier that publishes them.
-// m0 is reserved to the compiler, which uses it for nothing in these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
-    const unsigned la = __builtin_amdgcn_readfirstlane(
-        (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(la),
-                 "v"(voff), "s"(r)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // =========================================================================== dq
 
