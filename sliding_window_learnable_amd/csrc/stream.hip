@@ -14,13 +14,14 @@
 //   O^T += V^T P^T (bf16 MFMA).
 // At the end the sink's exp(s_h - max) joins the denominator exactly once.
 //
-// Pipeline: key tiles live in an LDS ring of three slots.  At the top of
-// iteration t the slots hold tiles t and t+1 and tile t+2 is in flight in
-// registers; a wave issues the S^T products of tile t+1 before the softmax
-// of tile t (so the matrix unit and the vector unit work at once), then the
-// PV products of tile t, then the max of tile t+1.  At the end of the
-// iteration tile t+2 is written to the slot freed by tile t-1 and tile t+3
-// is requested.  One barrier per tile.  Work-groups are issued longest-first
+// Pipeline: key tiles are copied from memory straight into an LDS ring of
+// four slots (buffer->LDS copies, no staging registers), three tiles ahead,
+// as rows whose 16-byte chunks are swizzled by row: K rows feed the A
+// operand of S^T directly and V^T is read with transposing LDS reads.  In
+// iteration t a wave issues the S^T products of tile t+1 before the
+// softmax of tile t (so the matrix unit and the vector unit work at once),
+// then the PV products of tile t; the copies of tile t+3 go to the slot
+// tile t-1 freed.  One barrier per tile.  Work-groups are issued longest-first
 // (the last query blocks have the most keys) with the (batch, KV head)
 // index fastest, so the blocks of one KV head share an XCD and its L2.
 #include "attn_device.h"
@@ -30,82 +31,14 @@ namespace swa {
 namespace {
 
 constexpr int kTile = 32;
-constexpr int kSlots = 3;
+constexpr int kSlots = 4;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr float kBig = 256.0f;           // 2^kRescaleSlack
 
 template <int D>
 struct StreamSmem {
-    bf16 k[kSlots][kTile][D + 8];        // row stride 2D+16 bytes: conflict-free fragment reads
-    bf16 vt[kSlots][D][kTile + 8];       // V^T, row stride 80 bytes: conflict-free fragment reads
-};
-
-// Loads one 32-key tile into registers (K as 16-byte row pieces, V as
-// 4-key x 8-dim quads) and writes it to a ring slot, V transposed.  The
-// buffer descriptor covers only the tile's rows that exist, so rows past
-// the end of the keys read as zeros.
-template <int D, int NT>
-struct TileLoader {
-    static constexpr int CH = D / 8;                       // 16-byte pieces per row
-    static constexpr int KPT = (kTile * CH + NT - 1) / NT;
-    static constexpr int VPT = (8 * CH + NT - 1) / NT;
-    bf16x8 kreg[KPT];
-    bf16x8 vreg[VPT][4];
-
-    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, size_t row_elems,
-                                         uint32_t rs, int S_kv, int T, int tid) {
-        const int rows = min(kTile, S_kv - kTile * T);
-        const uint32_t bytes = rows > 0 ? (uint32_t)rows * rs : 0u;
-        const rsrc_t kr = make_rsrc(kb + (size_t)kTile * T * row_elems, bytes);
-        const rsrc_t vr = make_rsrc(vb + (size_t)kTile * T * row_elems, bytes);
-        // Item counts are multiples of 64, so the guards are wave-uniform.
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < kTile * CH) kreg[i] = buf_load16(kr, (item / CH) * rs + 16 * (item % CH), 0);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < 8 * CH) {
-                const uint32_t vo = 4 * (item & 7) * rs + 16 * (item >> 3);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, vo + j * rs, 0);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(StreamSmem<D> &sm, int slot, int tid) const {
-        if (tid < kTile * CH) {                            // wave-uniform
-#pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-                const int item = tid + i * NT;
-                if (item < kTile * CH) *(bf16x8 *)&sm.k[slot][item / CH][8 * (item % CH)] = kreg[i];
-            }
-            // The data registers take the next tile's loads right after.
-            lds_settle(kreg);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < 8 * CH) {
-                const int kq = item & 7, ch = item >> 3;
-                u32x2 w[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16x4 x;
-                    x[0] = vreg[i][0][e];
-                    x[1] = vreg[i][1][e];
-                    x[2] = vreg[i][2][e];
-                    x[3] = vreg[i][3][e];
-                    w[e] = __builtin_bit_cast(u32x2, x);
-                    *(u32x2 *)&sm.vt[slot][8 * ch + e][4 * kq] = w[e];
-                }
-                // Written while this wave's PV products may still be running.
-                lds_settle(w);
-            }
-        }
-    }
+    bf16 k[kSlots][kTile][D];            // K rows, chunks swizzled by row
+    bf16 v[kSlots][kTile][D];            // V rows, chunks swizzled by row
 };
 
 template <int D, int NW>
@@ -113,7 +46,6 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S_q,
     int S_kv, int Hq, int Hkv, int W, int BG, int NB) {
-    constexpr int NT = NW * 64;
     __shared__ __align__(16) StreamSmem<D> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -145,29 +77,57 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     //   32T + 16(r>>3) + (r&7) + kbias
     const int kbias = 8 * hl - pq;
 
-    TileLoader<D, NT> ld;
     auto tile_keys_masked = [&](int T) {               // wave-uniform
         return kTile * T + kTile - 1 > p_first || kTile * T <= p_last - W;
     };
+    // Copies of one tile: 2 * 32 rows of 2D bytes in 1 KB instructions, IPW
+    // per wave (K first, then V); rows past the end of the keys land as zero.
+    constexpr int CPR = D / 8;                         // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                      // rows per instruction
+    constexpr int NI = 2 * kTile / RPI;                // instructions per tile
+    constexpr int IPW = NI / NW;
+    static_assert(IPW >= 1 && IPW * NW == NI, "copy split");
+    uint32_t dma_off[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+        const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
+        dma_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
+    }
+    auto stage = [&](int T, int slot) {
+        const int rows = min(kTile, S_kv - kTile * T);
+        const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * rs + D * 2 : 0u;
+        const size_t to = (size_t)kTile * T * row_elems;
+        const u32x4 kr = sgpr_rsrc(kb + to, bytes), vr = sgpr_rsrc(vb + to, bytes);
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int ii = wave * IPW + u;             // uniform
+            const bool is_k = ii < NI / 2;
+            bf16(*tile)[D] = is_k ? sm.k[slot] : sm.v[slot];
+            dma16(is_k ? kr : vr, tile[(ii % (NI / 2)) * RPI], dma_off[u]);
+        }
+    };
+    auto dma_wait = [&](bool newer) {
+        if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
+    const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
 
     for (int hh = wave; hh < G; hh += NW) {
         const int h = g * G + hh;
         if (hh != wave) lds_barrier();                 // previous head's reads are done
-        // Prologue: tiles 0 and 1 into slots 0 and 1, tile 2 in flight.
-        ld.load(kb, vb, row_elems, rs, S_kv, T_lo, tid);
-        ld.store(sm, 0, tid);
-        if (n_tiles > 1) {
-            ld.load(kb, vb, row_elems, rs, S_kv, T_lo + 1, tid);
-            ld.store(sm, 1, tid);
-        }
-        if (n_tiles > 2) ld.load(kb, vb, row_elems, rs, S_kv, T_lo + 2, tid);
-
         bf16x8 qf[D / 16];
         {
             const bf16 *qrow = q + (((size_t)b * S_q + min(i, S_q - 1)) * Hq + h) * D + 8 * hl;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) retire(qf[ks]);
         }
+        // Prologue: tiles 0, 1 (and 2, left in flight) into slots 0, 1, 2.
+        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
+        if (n_tiles > 2) dma_wait(true);
+        else dma_wait(false);
         const float s2 = sink[h] * kLog2e;
         float m = s2;                                  // running max seeded with the sink
         float l = 0.0f;                                // this lane's share of the real-token sum
@@ -176,10 +136,10 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
         auto qk = [&](int slot) {
-            const bf16 *krow = &sm.k[slot][score_row_key(lq)][8 * hl];
+            const bf16 *krow = sm.k[slot][arow_r];
             bf16x8 a[D / 16];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) a[ks] = *(const bf16x8 *)(krow + 16 * ks);
+            for (int ks = 0; ks < D / 16; ++ks) a[ks] = *(const bf16x8 *)(krow + 8 * ((2 * ks + hl) ^ arow_s));
             f32x16 sc = mfma32(a[0], qf[0], zero16());
 #pragma unroll
             for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], qf[ks], sc);
@@ -211,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             }
         };
 
-        lds_barrier();                                 // slots 0 and 1 staged
+        lds_barrier();                                 // slots 0 and 1 landed
         f32x16 s_cur = qk(0);
         if (tile_keys_masked(T_lo)) mask(s_cur, T_lo);
         // Nothing accumulated yet: the first tile only raises the max.
@@ -220,7 +180,9 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         for (int t = 0; t < n_tiles; ++t) {
             const int T = T_lo + t;
             const bool more = t + 1 < n_tiles;
-            if (t > 0) lds_barrier();                  // tile t+1 staged, tile t-1 released
+            if (t > 0) lds_barrier();                  // tile t+1 landed, tile t-1 released
+            const bool copy = t + 3 < n_tiles;
+            if (copy) stage(T + 3, (t + 3) % kSlots);  // into the slot tile t-1 freed
             // Past the last tile the product reads a stale slot and is discarded.
             f32x16 s_next = qk((t + 1) % kSlots);
 
@@ -247,12 +209,21 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) l += p[r];
             const bf16x8 pa = pack8(p, 0), pb = pack8(p, 1);
+            // O^T += V^T P^T: A row m = dim 32dt + m, k = key 16kk + 8hl + 0..7,
+            // from the V row tile by transposing reads of 4 keys each.
             const int slot = t % kSlots;
+            const bf16(*vt)[D] = sm.v[slot];
             bf16x8 va[D / 32][2];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                va[dt][0] = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][8 * hl];
-                va[dt][1] = *(const bf16x8 *)&sm.vt[slot][32 * dt + lq][16 + 8 * hl];
+                const int d = 32 * dt + tr_d, cc = d >> 3, half = (d >> 2) & 1;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
+                    const bf16x4 lo = lds_read_tr(&vt[r1][8 * (cc ^ swz<D>(r1)) + 4 * half]);
+                    const bf16x4 hi4 = lds_read_tr(&vt[r2][8 * (cc ^ swz<D>(r2)) + 4 * half]);
+                    va[dt][kk] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
             }
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
@@ -264,10 +235,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
                 if (tile_keys_masked(T + 1)) mask(s_next, T + 1);
                 s_cur = s_next;
             }
-            if (t + 2 < n_tiles) {
-                ld.store(sm, (t + 2) % kSlots, tid);
-                if (t + 3 < n_tiles) ld.load(kb, vb, row_elems, rs, S_kv, T + 3, tid);
-            }
+            dma_wait(copy);                            // tile t+2 landed (t+3 may be in flight)
         }
 
         // Sink joins the denominator once: l_total = sum_j e^{x_j - m} + e^{s_h - m}.
