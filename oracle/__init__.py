@@ -15,7 +15,8 @@ numpy arrays into contiguous float64 buffers, and states each call's key set:
   sits at position S_kv - S_q + i and sees 0 .. that position (same digest,
   混合注意力机制: global layers see the whole sequence);
 * ring decode -- see ``ring_decode``;
-* the gradients of the first two -- see ``attend_backward``.
+* the gradients of the first two -- see ``attend_backward``;
+* block maxima of the global layer's logits -- see ``block_max``.
 
 The sink term is described in the same digest, 前置知识 / 注意力sink偏置.
 """
@@ -60,6 +61,8 @@ def bind(path: str):
     lib.oracle_attend_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                            i64, i64, i64, i64, i64, i64]
     lib.oracle_attend_backward.restype = None
+    lib.oracle_block_max.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64]
+    lib.oracle_block_max.restype = None
     lib.oracle_count_window_pairs.argtypes = [i64, i64]
     lib.oracle_count_window_pairs.restype = i64
     lib.oracle_threads.argtypes = []
@@ -199,6 +202,23 @@ def attend_backward(q, k, v, sink, dout, window, lib=None):
         _dp(q), _dp(k), _dp(v), _dp(sink), _dp(dout), _dp(dq), _dp(dk), _dp(dv), _dp(dsink),
         B, S, Hq, Hkv, D, int(min(window, S)))
     return dq, dk, dv, dsink
+
+
+def block_max(q, k, block_k, lib=None):
+    """Largest scaled logit q_i . k_j / sqrt(D) over the visible pairs of each
+    (32-row query block, block_k-key block) of global causal attention with
+    the queries at the end of the keys; -inf for blocks with no visible pair.
+
+    q [B, S_q, Hq, D], k [B, S_kv, Hkv, D]
+    -> [B, Hq, ceil(S_q / 32), ceil(S_kv / block_k)] (float64)."""
+    q, k = _f64(q), _f64(k)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    assert Sq <= Skv and Hq % Hkv == 0 and block_k >= 1
+    out = np.empty((B, Hq, (Sq + 31) // 32, (Skv + block_k - 1) // block_k))
+    (lib or _load()).oracle_block_max(_dp(q), _dp(k), _dp(out), B, Sq, Skv, Hq, Hkv, D,
+                                      int(block_k))
+    return out
 
 
 def count_window_pairs(S: int, W: int) -> int:

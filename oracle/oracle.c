@@ -283,6 +283,45 @@ void oracle_attend_backward(const double *q, const double *k, const double *v,
     free(ds_part);
 }
 
+/* Block maxima of the scaled logits of global causal attention.
+ * Source: "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？| ICML 2026", §02
+ * (High Sparse): later sparse layers select tokens by block from the
+ * block-level scores the full-attention layer's FlashAttention pass produces.
+ * Reading: the block score is the largest scaled logit x_ij = q_i . k_j /
+ * sqrt(D) over the visible (row, key) pairs of the block -- the quantity the
+ * pass already forms per tile -- in the units of the sink s_h; -inf when the
+ * block has no visible pair.  Query blocks are 32 rows, key blocks bk keys;
+ * queries at the end of the keys (row i at position S_kv - S_q + i).
+ *   q [B,S_q,Hq,D], k [B,S_kv,Hkv,D] -> bmax [B, Hq, ceil(S_q/32), ceil(S_kv/bk)]
+ */
+void oracle_block_max(const double *q, const double *k, double *bmax, int64_t B,
+                      int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,
+                      int64_t bk)
+{
+    const int64_t G = Hq / Hkv, nqb = (S_q + 31) / 32, nkb = (S_kv + bk - 1) / bk;
+    const double scale = 1.0 / sqrt((double)D);
+    const int64_t n = B * Hq * nqb * nkb;
+    for (int64_t e = 0; e < n; ++e) bmax[e] = -INFINITY;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / G;
+            double *blk = bmax + (b * Hq + h) * nqb * nkb;
+            for (int64_t i = 0; i < S_q; ++i) {
+                const int64_t pos = S_kv - S_q + i;
+                const double *qi = q + ((b * S_q + i) * Hq + h) * D;
+                for (int64_t j = 0; j <= pos; ++j) {
+                    const double *kj = k + ((b * S_kv + j) * Hkv + g) * D;
+                    double x = 0.0;
+                    for (int64_t d = 0; d < D; ++d) x += qi[d] * kj[d];
+                    x *= scale;
+                    double *slot = blk + (i / 32) * nkb + j / bk;
+                    if (x > *slot) *slot = x;
+                }
+            }
+        }
+}
+
 /* Number of (query, key) pairs a causal window-W layer attends over S tokens:
  * enumerated one row at a time (used to check closed-form FLOP counts). */
 int64_t oracle_count_window_pairs(int64_t S, int64_t W)

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_backward as bwd
+from tests import test_oracle_block_max as blk
 from tests import test_oracle_pins as pins
 
 MUTANTS = {
@@ -45,6 +46,14 @@ MUTANTS = {
     "dq uses q": ("dqi[d] += scale * dx * kj[d];", "dqi[d] += scale * dx * qi[d];"),
     "backward misses the diagonal key": ("const int64_t n = i - lo + 1;",
                                          "const int64_t n = i - lo;"),
+    # block maxima
+    "block max misses the diagonal": ("for (int64_t j = 0; j <= pos; ++j) {",
+                                      "for (int64_t j = 0; j < pos; ++j) {"),
+    "block max unscaled": ("    x *= scale;\n                    double *slot", "    x *= 1.0;\n                    double *slot"),
+    "block max row blocks of 16": ("double *slot = blk + (i / 32) * nkb + j / bk;",
+                                   "double *slot = blk + (i / 16 < nqb ? i / 16 : nqb - 1) * nkb + j / bk;"),
+    "block max aligned at the start": ("const int64_t pos = S_kv - S_q + i;\n                const double *qi",
+                                       "const int64_t pos = i;\n                const double *qi"),
 }
 
 PINS = [
@@ -70,6 +79,11 @@ PINS = [
     (bwd.test_gqa_is_repeated_kv_heads_summed, {}),
     (bwd.test_sink_gradient_from_forward_outputs, dict(W=3)),
     (bwd.test_dv_is_attention_weights_times_dout, {}),
+    (blk.test_block_max_equals_torch, dict(Sq=70, Skv=90, bk=64)),
+    (blk.test_block_max_brute_force_loops, {}),
+    (blk.test_row_max_brackets_lse, {}),
+    (blk.test_zero_keys_give_the_causal_block_pattern, {}),
+    (blk.test_heads_of_a_group_with_equal_queries_agree, {}),
 ]
 
 
