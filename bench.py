@@ -196,14 +196,22 @@ def bench_hybrid(args, swa, acc, torch):
         q, k, v, s = layers[5]
         swa.global_sink_attn(q, k, v, s, out=out, lse=lse)
 
+    q5, k5, v5, s5 = layers[5]
+    bmax = torch.empty((B, Hq, S // 32, S // 128), device="cuda", dtype=torch.float32)
+
+    def ga_layer_blocks(i):
+        swa.global_sink_attn_block_max(q5, k5, v5, s5, block_k=128, out=out, lse=lse,
+                                       block_max=bmax)
+
     log("hybrid 5:1 at S=65536")
     ms_swa5 = timed(swa_layers, 5, 1)
     ms_ga = timed(ga_layer, 3, 1)
+    ms_ga_blk = timed(ga_layer_blocks, 3, 1)
     f_swa = acc.prefill_flops(B, S, Hq, D, W)
     f_ga = acc.global_flops(B, S, S, Hq, D)
     compute_red, kv_red = acc.hybrid_ratios(S, W, 5)
     compute_red7, kv_red7 = acc.hybrid_ratios(S, W, 7)
-    del layers
+    del layers, q5, k5, v5, s5, bmax
     torch.cuda.empty_cache()
     return {
         "workload": "5 x swa_sink_prefill (window 128) + 1 x global_sink_attn, B=1 S=65536 "
@@ -218,6 +226,9 @@ def bench_hybrid(args, swa, acc, torch):
         "attention_compute_reduction_vs_6_global": compute_red,
         "kv_cache_reduction_vs_6_global": kv_red,
         "measured_time_reduction_vs_6_global": 6 * ms_ga / (ms_swa5 + ms_ga),
+        # the global layer with the block-score side output (32-row x 128-key blocks)
+        "global_layer_with_block_max_ms": ms_ga_blk,
+        "block_max_overhead": ms_ga_blk / ms_ga - 1.0,
         # 7:1 schedule (Pro): the same two layer types, 7 SWA layers per global one
         "schedule_7to1": {
             "stack_ms": 7 * ms_swa5 / 5 + ms_ga,

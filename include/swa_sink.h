@@ -140,6 +140,30 @@ SWA_API int global_sink_attn(const void *q, const void *k, const void *v, const 
                      void *stream);
 
 /*
+ * global_sink_attn plus a block-score side output: for every query head h,
+ * 32-row query block qb and key block kb of block_k keys,
+ *   block_max[b, h, qb, kb] = max over the visible (row i, key j) of the
+ *                             block of q_i . k_j / sqrt(D)   (-inf if none),
+ * the scaled logit in the units of the sink s_h, as the full-attention pass
+ * forms it tile by tile.  Source: "小米罗福莉：MiMo-V2.5如何做到又快又强又
+ * 便宜？| ICML 2026", §02 (High Sparse: sparse layers select tokens by
+ * block from the block-level scores of the full-attention layer's
+ * FlashAttention pass, at no extra cost).
+ *
+ *   block_max  float32 [B, Hq, ceil(S_q / 32), ceil(S_kv / block_k)],
+ *              every element written (the caller need not clear it)
+ *   block_k    key block size: a positive multiple of 32 (else SWA_ERR_SHAPE)
+ * Other arguments, layouts and results as for global_sink_attn (queries at
+ * the end of the keys); out and lse are bit-identical to it.  bf16 only
+ * (SWA_ERR_UNSUPPORTED for float32); no workspace (the prefill-shaped
+ * streaming kernel serves every S_q).
+ */
+SWA_API int global_sink_attn_block_max(const void *q, const void *k, const void *v,
+                                       const float *sink, void *out, float *lse,
+                                       float *block_max, int block_k, int B, int Hq, int Hkv,
+                                       int S_q, int S_kv, int D, int dtype, void *stream);
+
+/*
  * Gradients of swa_sink_prefill (window < S) or of causal global attention
  * with a sink (window >= S, S_q == S_kv == S) for an upstream gradient dout:
  * dq, dk, dv and the gradient of the learnable sink.

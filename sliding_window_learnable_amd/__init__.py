@@ -22,6 +22,7 @@ __all__ = [
     "swa_sink_decode",
     "global_sink_attn",
     "global_sink_attn_workspace_bytes",
+    "global_sink_attn_block_max",
     "swa_sink_backward",
     "swa_sink_backward_workspace_bytes",
     "SwaError",
@@ -145,6 +146,33 @@ def global_sink_attn(q, k, v, sink, out=None, lse=None, workspace=None, want_lse
           _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, D, _ptr(workspace), wbytes,
           dt, _stream(stream))
     return out, lse
+
+
+def global_sink_attn_block_max(q, k, v, sink, block_k=128, out=None, lse=None, block_max=None,
+                               want_lse: bool = True, stream=None):
+    """global_sink_attn (bf16) plus, for every query head, 32-row query block
+    and ``block_k``-key block, the largest scaled logit q.k/sqrt(D) over the
+    block's visible pairs (-inf when none).
+
+    Returns (out, lse, block_max [B, Hq, ceil(S_q/32), ceil(S_kv/block_k)]).
+    """
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    if block_max is None:
+        block_max = torch.empty((B, Hq, -(-Sq // 32), -(-Skv // block_k)), device=q.device,
+                                dtype=torch.float32)
+    _check_device(q, k, v, sink, out, lse, block_max)
+    dt = _dtype_code(q, k, v, out)
+    _call(_lib.load().global_sink_attn_block_max, "global_sink_attn_block_max", _ptr(q), _ptr(k),
+          _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(block_max), block_k, B, Hq, Hkv, Sq,
+          Skv, D, dt, _stream(stream))
+    return out, lse, block_max
 
 
 def swa_sink_backward_workspace_bytes(B, Hq, S) -> int:

@@ -19,6 +19,7 @@ EXPORTS = (
     "swa_sink_decode",
     "global_sink_attn_workspace_bytes",
     "global_sink_attn",
+    "global_sink_attn_block_max",
     "swa_sink_backward_workspace_bytes",
     "swa_sink_backward",
     "swa_sink_strerror",
@@ -52,6 +53,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.global_sink_attn_workspace_bytes.restype = sz
     lib.global_sink_attn.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, sz, i, vp]
     lib.global_sink_attn.restype = i
+    lib.global_sink_attn_block_max.argtypes = [vp, vp, vp, fp, vp, fp, fp, i, i, i, i, i, i, i,
+                                               i, vp]
+    lib.global_sink_attn_block_max.restype = i
     lib.swa_sink_backward_workspace_bytes.argtypes = [i, i, i]
     lib.swa_sink_backward_workspace_bytes.restype = sz
     lib.swa_sink_backward.argtypes = [vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp,

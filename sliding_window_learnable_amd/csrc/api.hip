@@ -107,6 +107,27 @@ int global_sink_attn(const void *q, const void *k, const void *v, const float *s
     return status_of(swa::launch_stream_bf16(a, st));
 }
 
+int global_sink_attn_block_max(const void *q, const void *k, const void *v, const float *sink,
+                               void *out, float *lse, float *block_max, int block_k, int B,
+                               int Hq, int Hkv, int S_q, int S_kv, int D, int dtype,
+                               void *stream) {
+    if (!q || !k || !v || !sink || !out || !block_max) return SWA_ERR_NULL;
+    if (S_q < 0 || S_kv < 0 || S_q > S_kv || block_k < 32 || block_k % 32 != 0)
+        return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4) || !aligned(block_max, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+
+    swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
+    return status_of(
+        swa::launch_stream_bf16_block_max(a, block_max, block_k, static_cast<hipStream_t>(stream)));
+}
+
 size_t swa_sink_backward_workspace_bytes(int B, int Hq, int S) {
     if (B < 1 || Hq < 1 || S < 1) return 0;
     return swa::backward_workspace_bytes(B, Hq, S);

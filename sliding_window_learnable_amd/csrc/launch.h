@@ -37,6 +37,11 @@ hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream);
 // bf16 banded / causal attention streaming key tiles through LDS: any window,
 // queries aligned to the end of the keys (row i at position S_kv - S + i).
 hipError_t launch_stream_bf16(const PrefillArgs &a, hipStream_t stream);
+// The same, also writing per (query head, 32-row block, block_k-key block)
+// the largest scaled logit over the block's visible pairs to bmax
+// [B, Hq, ceil(S/32), ceil(S_kv/block_k)] (block_k a multiple of 32).
+hipError_t launch_stream_bf16_block_max(const PrefillArgs &a, float *bmax, int block_k,
+                                        hipStream_t stream);
 
 // bf16 decode over a ring cache (split-free).
 hipError_t launch_ring_decode_bf16(const DecodeArgs &a, hipStream_t stream);

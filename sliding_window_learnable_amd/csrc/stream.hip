@@ -41,11 +41,18 @@ struct StreamSmem {
     bf16 v[kSlots][kTile][D];            // V rows, chunks swizzled by row
 };
 
-template <int D, int NW>
+// BLK: also write, per (query head, 32-row block, key block of 32 rk keys),
+// the largest scaled logit q.k/sqrt(D) over the block's visible pairs
+// (-inf when none) to bmax [B, Hq, NB, NKB].  The max is taken on the
+// softmax's own exponent arguments t = s c - m (one v_max per score, no
+// canonicalisation), m added back per tile; each lane keeps a running max
+// over the tiles of the current key block, reduced across the wave once
+// per key block.
+template <int D, int NW, bool BLK>
 __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S_q,
-    int S_kv, int Hq, int Hkv, int W, int BG, int NB) {
+    int S_kv, int Hq, int Hkv, int W, int BG, int NB, float *__restrict__ bmax, int rk, int NKB) {
     __shared__ __align__(16) StreamSmem<D> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -171,6 +178,25 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             }
         };
 
+        // Block maxima: running max of the raw scores of this lane, per key block.
+        float bm_run = -INFINITY;
+        float *brow = BLK ? bmax + (((size_t)b * Hq + h) * NB + qb) * NKB : nullptr;
+        // tmax: max over this lane's exponent arguments of tile T (log2
+        // units, relative to mu); bm_run is kept in absolute log2 units.
+        auto block_step = [&](float tmax, float mu, int T) {
+            bm_run = fmaxf(bm_run, tmax + mu);
+            if ((T + 1) % rk == 0 || T == T_hi) {      // last tile of a key block (uniform)
+                float w = bm_run;
+#pragma unroll
+                for (int sh = 1; sh < 64; sh <<= 1) w = fmaxf(w, __shfl_xor(w, sh));
+                if (lane == 0) brow[T / rk] = w == -INFINITY ? -INFINITY : w * kLn2;
+                bm_run = -INFINITY;
+            }
+        };
+        if (BLK) {                                     // key blocks past the diagonal see nothing
+            for (int kb = T_hi / rk + 1 + lane; kb < NKB; kb += 64) brow[kb] = -INFINITY;
+        }
+
         lds_barrier();                                 // slots 0 and 1 landed
         f32x16 s_cur = qk(0);
         if (tile_keys_masked(T_lo)) mask(s_cur, T_lo);
@@ -192,20 +218,30 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             // exact max, rescale, recompute.  A column whose max is still
             // -inf uses an offset that sends any finite score to +inf.
             f32x16 p;
-            {
-                const float mu = (m == -INFINITY) ? -3.0e38f : m;
+            float tmax = -INFINITY, mu = (m == -INFINITY) ? -3.0e38f : m;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
+            for (int r = 0; r < 16; r += 2) {
+                const float ta = fmaf(s_cur[r], c, -mu), tb = fmaf(s_cur[r + 1], c, -mu);
+                p[r] = __builtin_amdgcn_exp2f(ta);
+                p[r + 1] = __builtin_amdgcn_exp2f(tb);
+                if (BLK) tmax = fmaxf(tmax, fmaxf(ta, tb));   // v_max3
             }
             float pmax = fmaxf(p[0], p[1]);
 #pragma unroll
             for (int r = 2; r < 16; r += 2) pmax = fmaxf(pmax, fmaxf(p[r], p[r + 1]));
             if (__ballot(pmax > kBig) != 0) {
                 maybe_rescale(tile_max(s_cur));
-                const float mu = (m == -INFINITY) ? -3.0e38f : m;
+                mu = (m == -INFINITY) ? -3.0e38f : m;
+                tmax = -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -mu));
+                for (int r = 0; r < 16; r += 2) {
+                    const float ta = fmaf(s_cur[r], c, -mu), tb = fmaf(s_cur[r + 1], c, -mu);
+                    p[r] = __builtin_amdgcn_exp2f(ta);
+                    p[r + 1] = __builtin_amdgcn_exp2f(tb);
+                    if (BLK) tmax = fmaxf(tmax, fmaxf(ta, tb));
+                }
             }
+            if (BLK) block_step(tmax, mu, T);
 #pragma unroll
             for (int r = 0; r < 16; ++r) l += p[r];
             const bf16x8 pa = pack8(p, 0), pb = pack8(p, 1);
@@ -261,31 +297,40 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     }
 }
 
-template <int D, int NW>
-hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
+template <int D, int NW, bool BLK>
+hipError_t launch(const PrefillArgs &a, float *bmax, int block_k, hipStream_t stream) {
     const int BG = a.B * a.Hkv;
     const int NB = (a.S + kTile - 1) / kTile;
     const long n_wg = (long)BG * NB;
-    hipLaunchKernelGGL((stream_attn_kernel<D, NW>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
-                       (bf16 *)a.out, a.lse, a.S, a.S_kv, a.Hq, a.Hkv, a.window, BG, NB);
+    const int rk = block_k / kTile, NKB = (a.S_kv + block_k - 1) / block_k;
+    hipLaunchKernelGGL((stream_attn_kernel<D, NW, BLK>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
+                       stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
+                       (bf16 *)a.out, a.lse, a.S, a.S_kv, a.Hq, a.Hkv, a.window, BG, NB, bmax, rk,
+                       NKB);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
+template <int D, bool BLK>
+hipError_t launch_d(const PrefillArgs &a, float *bmax, int block_k, hipStream_t stream) {
     switch (waves_for_group(a.Hq / a.Hkv)) {
-    case 8: return launch<D, 8>(a, stream);
-    case 4: return launch<D, 4>(a, stream);
-    case 2: return launch<D, 2>(a, stream);
-    default: return launch<D, 1>(a, stream);
+    case 8: return launch<D, 8, BLK>(a, bmax, block_k, stream);
+    case 4: return launch<D, 4, BLK>(a, bmax, block_k, stream);
+    case 2: return launch<D, 2, BLK>(a, bmax, block_k, stream);
+    default: return launch<D, 1, BLK>(a, bmax, block_k, stream);
     }
 }
 
 }  // namespace
 
 hipError_t launch_stream_bf16(const PrefillArgs &a, hipStream_t stream) {
-    return a.D == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
+    return a.D == 64 ? launch_d<64, false>(a, nullptr, kTile, stream)
+                     : launch_d<128, false>(a, nullptr, kTile, stream);
+}
+
+hipError_t launch_stream_bf16_block_max(const PrefillArgs &a, float *bmax, int block_k,
+                                        hipStream_t stream) {
+    return a.D == 64 ? launch_d<64, true>(a, bmax, block_k, stream)
+                     : launch_d<128, true>(a, bmax, block_k, stream);
 }
 
 }  // namespace swa

@@ -177,8 +177,32 @@ def test_backward_rejects(lib, kw, code):
 
 
 def test_backward_workspace_and_empty(lib):
-    # D_i per (b, h, row) plus one sink-gradient partial per 32 rows, float32
+    # D_i and lse*log2(e) per (b, h, row) plus one sink-gradient partial per 32 rows, float32
     assert lib.swa_sink_backward_workspace_bytes(2, 64, 1000) == 4 * 2 * 64 * (2 * 1000 + 32)
     assert lib.swa_sink_backward_workspace_bytes(0, 64, 1000) == 0
     assert bwd(lib, B=0, ws=None, wsb=0) == _lib.SWA_OK
     assert bwd(lib, S=0, ws=None, wsb=0) == _lib.SWA_OK
+
+
+def bmax(lib, q=P, k=P, v=P, sink=P, out=P, lse=None, bm=P, bk=128, B=1, Hq=8, Hkv=1, Sq=64,
+         Skv=64, D=128, dtype=1):
+    return lib.global_sink_attn_block_max(q, k, v, sink, out, lse, bm, bk, B, Hq, Hkv, Sq, Skv, D,
+                                          dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(bm=None), _lib.SWA_ERR_NULL),
+    (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(bk=0), _lib.SWA_ERR_SHAPE), (dict(bk=48), _lib.SWA_ERR_SHAPE),
+    (dict(bk=16), _lib.SWA_ERR_SHAPE), (dict(Sq=65), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE),
+    (dict(dtype=0), _lib.SWA_ERR_UNSUPPORTED), (dict(D=96), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(bm=P + 2), _lib.SWA_ERR_UNSUPPORTED), (dict(q=P + 8), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_block_max_rejects(lib, kw, code):
+    assert bmax(lib, **kw) == code
+
+
+def test_block_max_empty_is_noop(lib):
+    assert bmax(lib, B=0) == _lib.SWA_OK
+    assert bmax(lib, Sq=0) == _lib.SWA_OK
