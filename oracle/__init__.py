@@ -56,11 +56,13 @@ def bind(path: str):
                                        i64, i64, i64, i64, i64]
     lib.oracle_attend_rows.restype = None
     lib.oracle_ring_decode.argtypes = [dp, dp, dp, dp, ip, dp, dp,
-                                       i64, i64, i64, i64, i64, i64]
+                                       i64, i64, i64, i64, i64, i64, i64]
     lib.oracle_ring_decode.restype = None
     lib.oracle_attend_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                            i64, i64, i64, i64, i64, i64]
     lib.oracle_attend_backward.restype = None
+    lib.oracle_rope.argtypes = [dp, ip, dp, i64, i64, i64, ctypes.c_double]
+    lib.oracle_rope.restype = None
     lib.oracle_block_max.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, i64]
     lib.oracle_block_max.restype = None
     lib.oracle_count_window_pairs.argtypes = [i64, i64]
@@ -162,13 +164,14 @@ def global_attn(q, k, v, sink):
     return out.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
 
 
-def ring_decode(q, kcache, vcache, sink, cache_len=None):
+def ring_decode(q, kcache, vcache, sink, cache_len=None, window=None):
     """Decode T new query tokens per sequence against a W-slot ring cache.
 
     q [B, T, Hq, D]; kcache/vcache [B, Hkv, W, D] with the key of absolute
     position P in slot P mod W; cache_len [B] = tokens written so far
-    including the T new ones (None: every ring is exactly full, L = W).
-    Query t is at position L - T + t and sees positions max(0, L-W) .. itself.
+    including the T new ones (None: every ring is exactly full, L = W);
+    window = keys per query (default W, at most W).  Query t is at position
+    p = L - T + t and sees positions max(0, L-W, p-window+1) .. p.
     Returns out [B, T, Hq, D], lse [B, T, Hq] (float64).
     """
     q, kcache, vcache, sink = _f64(q), _f64(kcache), _f64(vcache), _f64(sink)
@@ -179,9 +182,46 @@ def ring_decode(q, kcache, vcache, sink, cache_len=None):
     assert cl.shape == (B,)
     out = np.zeros((B, T, Hq, D), dtype=np.float64)
     lse = np.zeros((B, T, Hq), dtype=np.float64)
+    wnd = W if window is None else int(window)
+    assert 1 <= wnd <= W
     _load().oracle_ring_decode(_dp(q), _dp(kcache), _dp(vcache), _dp(sink), _ip(cl),
-                               _dp(out), _dp(lse), B, T, Hq, Hkv, W, D)
+                               _dp(out), _dp(lse), B, T, Hq, Hkv, W, D, wnd)
     return out, lse
+
+
+def rope(x, pos, theta):
+    """Rotary position embedding of x [n, H, D] at absolute positions pos [n]
+    (dimension i paired with i + D/2, angle pos * theta^(-2i/D))."""
+    x = _f64(x)
+    n, H, D = x.shape
+    pos = _i64(pos)
+    assert pos.shape == (n,) and D % 2 == 0
+    y = np.empty_like(x)
+    _load().oracle_rope(_dp(x), _ip(pos), _dp(y), n, H, D, float(theta))
+    return y
+
+
+def rope_append(q, k_new, v_new, kcache, vcache, cache_len_old, theta):
+    """One decode step's preparation: RoPE on the T new queries and keys at
+    positions L_old + t, and the keys (rotated) and values written to ring
+    slots (L_old + t) mod W.  q [B, T, Hq, D]; k_new, v_new [B, T, Hkv, D];
+    kcache, vcache [B, Hkv, W, D] (copies are updated and returned);
+    cache_len_old [B] = tokens in the cache before the step.
+    Returns (q_rot, kcache, vcache)."""
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(kcache).copy(), _f64(vcache).copy()
+    B, T, Hq, D = q.shape
+    Hkv, W = kc.shape[1], kc.shape[2]
+    lo = _i64(cache_len_old)
+    pos = (lo[:, None] + np.arange(T)[None, :]).reshape(-1)
+    q_rot = rope(q.reshape(B * T, Hq, D), pos, theta).reshape(B, T, Hq, D)
+    k_rot = rope(k_new.reshape(B * T, Hkv, D), pos, theta).reshape(B, T, Hkv, D)
+    for b in range(B):
+        for t in range(T):
+            slot = (int(lo[b]) + t) % W
+            kc[b, :, slot] = k_rot[b, t]
+            vc[b, :, slot] = v_new[b, t]
+    return q_rot, kc, vc
 
 
 def attend_backward(q, k, v, sink, dout, window, lib=None):

@@ -133,13 +133,17 @@ void oracle_attend_rows(const double *q, const int64_t *qb, const int64_t *lo,
  *
  *   q [B, T, Hq, D]   kc, vc [B, Hkv, W, D]   out [B, T, Hq, D]   lse [B, T, Hq]
  *   cache_len [B]: L_b = tokens written so far, including the T new ones.
- * Query t sits at position p = L - T + t and sees the positions
- * max(0, L-W) .. p: everything older than L-W has been overwritten.
+ * The ring has W slots (position P in slot P mod W); the attention window is
+ * Wnd keys (Wnd <= W).  Query t sits at position p = L - T + t and sees the
+ * positions max(0, L-W, p-Wnd+1) .. p: everything older than L-W has been
+ * overwritten, and the window reaches back Wnd-1 positions.  With Wnd = W
+ * the bound is max(0, L-W); a ring of Wnd + T - 1 slots gives every query
+ * its full window (none of them needs a position older than L-W).
  */
 void oracle_ring_decode(const double *q, const double *kc, const double *vc,
                         const double *sink, const int64_t *cache_len,
                         double *out, double *lse, int64_t B, int64_t T,
-                        int64_t Hq, int64_t Hkv, int64_t W, int64_t D)
+                        int64_t Hq, int64_t Hkv, int64_t W, int64_t D, int64_t Wnd)
 {
     const int64_t G = Hq / Hkv;
 #pragma omp parallel
@@ -155,8 +159,9 @@ void oracle_ring_decode(const double *q, const double *kc, const double *vc,
                     const int64_t L = cache_len[b];
                     const int64_t p = L - T + t;
                     const int64_t oldest = L - W > 0 ? L - W : 0;
+                    const int64_t first = p - Wnd + 1 > oldest ? p - Wnd + 1 : oldest;
                     int64_t n = 0;
-                    for (int64_t P = oldest; P <= p; ++P) {
+                    for (int64_t P = first; P <= p; ++P) {
                         const int64_t slot = P % W;
                         const int64_t off = ((b * Hkv + g) * W + slot) * D;
                         kr[n] = kc + off;
@@ -281,6 +286,32 @@ void oracle_attend_backward(const double *q, const double *k, const double *v,
         dsink[h] = t;
     }
     free(ds_part);
+}
+
+/* Rotary position embedding of n rows of H heads at absolute positions pos.
+ * Source: "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？| ICML 2026", Q&A on
+ * RoPE (positions keep increasing as the window slides: cached keys carry
+ * their absolute positions).  Reading: the standard rotary embedding over
+ * the whole head, dimension i paired with i + D/2, angle pos * theta^(-2i/D):
+ *   y[i]       = x[i] cos(a) - x[i+D/2] sin(a)
+ *   y[i + D/2] = x[i+D/2] cos(a) + x[i] sin(a)
+ *   x, y [n, H, D]   pos [n]
+ */
+void oracle_rope(const double *x, const int64_t *pos, double *y, int64_t n, int64_t H,
+                 int64_t D, double theta)
+{
+    const int64_t half = D / 2;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < half; ++i) {
+            const double a = (double)pos[r] * pow(theta, -2.0 * (double)i / (double)D);
+            const double cs = cos(a), sn = sin(a);
+            for (int64_t h = 0; h < H; ++h) {
+                const double *xr = x + (r * H + h) * D;
+                double *yr = y + (r * H + h) * D;
+                yr[i] = xr[i] * cs - xr[i + half] * sn;
+                yr[i + half] = xr[i + half] * cs + xr[i] * sn;
+            }
+        }
 }
 
 /* Block maxima of the scaled logits of global causal attention.

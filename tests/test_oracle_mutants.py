@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_backward as bwd
 from tests import test_oracle_block_max as blk
 from tests import test_oracle_pins as pins
+from tests import test_oracle_rope_ring as rr
 
 MUTANTS = {
     "lse drops the sink": ("*lse_out = M + log(Z + E);", "*lse_out = M + log(Z);"),
@@ -52,6 +53,12 @@ MUTANTS = {
     "block max unscaled": ("    x *= scale;\n                    double *slot", "    x *= 1.0;\n                    double *slot"),
     "block max row blocks of 16": ("double *slot = blk + (i / 32) * nkb + j / bk;",
                                    "double *slot = blk + (i / 16 < nqb ? i / 16 : nqb - 1) * nkb + j / bk;"),
+    "rope frequency exponent sign": ("pow(theta, -2.0 * (double)i / (double)D)",
+                                     "pow(theta, 2.0 * (double)i / (double)D)"),
+    "rope rotation sign": ("yr[i] = xr[i] * cs - xr[i + half] * sn;",
+                           "yr[i] = xr[i] * cs + xr[i + half] * sn;"),
+    "ring window one key short": ("const int64_t first = p - Wnd + 1 > oldest ? p - Wnd + 1 : oldest;",
+                                  "const int64_t first = p - Wnd + 2 > oldest ? p - Wnd + 2 : oldest;"),
     "block max aligned at the start": ("const int64_t pos = S_kv - S_q + i;\n                const double *qi",
                                        "const int64_t pos = i;\n                const double *qi"),
 }
@@ -84,6 +91,9 @@ PINS = [
     (blk.test_row_max_brackets_lse, {}),
     (blk.test_zero_keys_give_the_causal_block_pattern, {}),
     (blk.test_heads_of_a_group_with_equal_queries_agree, {}),
+    (rr.test_rope_equals_complex_rotation, dict(theta=10000.0)),
+    (rr.test_rope_invariants, {}),
+    (rr.test_rollback_ring_gives_full_windows, dict(R=10, W=5, T=3)),
 ]
 
 
