@@ -176,6 +176,42 @@ def bench_decode(args, swa, acc, torch):
         del sets, outs, lses
         torch.cuda.empty_cache()
     res["time_ratio_T4_over_T1"] = res["T_q=4"]["us_per_call"] / res["T_q=1"]["us_per_call"]
+
+    # MTP with rollback: RoPE + ring append of 1 + 3 tokens, then decode in
+    # rings of W + T - 1 = 131 slots (every draft sees its full window).
+    T, R = 4, W + 3
+    sets = [inputs.ring_inputs(3, 10 + layer, B, T, Hq, Hkv, R, D, torch.bfloat16, "cuda")
+            for layer in range(nsets)]
+    news = [(inputs.ring_inputs(3, 20 + layer, B, T, Hq, Hkv, 1, D, torch.bfloat16, "cuda")[0],
+             torch.randn((B, T, Hkv, D), device="cuda").to(torch.bfloat16),
+             torch.randn((B, T, Hkv, D), device="cuda").to(torch.bfloat16)) for layer in range(nsets)]
+    lens_old = inputs.cache_lengths(B, R, 1 << 20, 33).to("cuda")
+    lens = lens_old + T
+    qrot = [torch.empty_like(n[0]) for n in news]
+    outs = [torch.empty_like(n[0]) for n in news]
+
+    def append(i):
+        s_, n_ = sets[i % nsets], news[i % nsets]
+        swa.swa_sink_rope_append(n_[0], n_[1], n_[2], s_[1], s_[2], lens_old, 1e6,
+                                 q_rot=qrot[i % nsets])
+
+    def decode_ring(i):
+        s_ = sets[i % nsets]
+        swa.swa_sink_decode_ring(qrot[i % nsets], s_[1], s_[2], s_[3], W, lens,
+                                 out=outs[i % nsets], want_lse=False)
+
+    steps = max(200, 10 * args.steps)
+    log("rollback ring: append + decode, %d calls each" % steps)
+    ms_a = timed(append, steps, 200)
+    ms_d = timed(decode_ring, steps, 200)
+    nbytes = acc.decode_bytes(B, T, Hq, Hkv, R, D)
+    res["rollback_ring_T_q=4"] = dict(
+        ring_slots=R, window=W, append_us=ms_a * 1e3, decode_us=ms_d * 1e3,
+        decode_hbm_gbs=nbytes / (ms_d * 1e-3) / 1e9,
+        decode_frac_hbm_peak=nbytes / (ms_d * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+        step_us=(ms_a + ms_d) * 1e3)
+    del sets, news, qrot, outs
+    torch.cuda.empty_cache()
     return res
 
 

@@ -114,6 +114,52 @@ SWA_API int swa_sink_decode(const void *q, const void *kcache, const void *vcach
                     void *stream);
 
 /*
+ * Ring decode with the attention window separate from the ring size, for
+ * MTP draft verification with rollback.  Source: technical-report digest,
+ * 前置知识 / 多token预测 (1 + 3 draft tokens verified in one pass) and the
+ * pwwt.cn article on MiMo-V2-Flash, §1.1 (fixed-size SWA cache).
+ *
+ *   kcache, vcache [B, Hkv, ring, D]: position P in slot P mod ring
+ *   cache_len [B] (device, int32; NULL: L = ring): tokens written so far,
+ *                 including the T_q new ones
+ * Query t sits at position p = L - T_q + t and sees positions
+ * max(0, L - ring, p - window + 1) .. p.  With ring >= window + T_q - 1
+ * every query sees its full window however many drafts the previous step
+ * rejected (the caller rolls back by lowering its token count; the rejected
+ * slots are rewritten by the next append).  ring == window is exactly
+ * swa_sink_decode.  Requires window >= 1, ring >= window, T_q <= ring.
+ * Other arguments and results as for swa_sink_decode.
+ */
+SWA_API int swa_sink_decode_ring(const void *q, const void *kcache, const void *vcache,
+                                 const float *sink, void *out, float *lse, int B, int Hq,
+                                 int Hkv, int T_q, int window, int ring, int D,
+                                 const int32_t *cache_len, int dtype, void *stream);
+
+/*
+ * The step before ring decode: rotary position embedding of the T_q new
+ * queries and keys at their absolute positions, and the rotated keys and the
+ * values written to their ring slots.  Source: "小米罗福莉：MiMo-V2.5如何做到
+ * 又快又强又便宜？| ICML 2026", Q&A on RoPE (positions keep increasing as the
+ * window slides: cached keys carry absolute positions).
+ *
+ *   q, q_rot [B, T_q, Hq, D]   k_new, v_new [B, T_q, Hkv, D]   (dtype)
+ *   kcache, vcache [B, Hkv, ring, D]
+ *   cache_len_old [B] (device, int32; NULL: 0): tokens in the cache before
+ *                 this step; token t is at position P = cache_len_old + t
+ * Rotation: dimension i (< D/2) pairs with i + D/2 at angle
+ * P * rope_theta^(-2i/D):  y_i = x_i cos - x_{i+D/2} sin,
+ * y_{i+D/2} = x_{i+D/2} cos + x_i sin (angles reduced in double precision,
+ * applied in fp32, rounded to dtype).  q_rot may be q (in place); the keys
+ * and values of token t go to slot P mod ring.  Requires T_q <= ring and
+ * rope_theta > 1 (else SWA_ERR_SHAPE / SWA_ERR_UNSUPPORTED).  The caller
+ * then decodes with cache_len_old + T_q tokens.
+ */
+SWA_API int swa_sink_rope_append(const void *q, const void *k_new, const void *v_new,
+                                 void *q_rot, void *kcache, void *vcache,
+                                 const int32_t *cache_len_old, int B, int Hq, int Hkv, int T_q,
+                                 int ring, int D, double rope_theta, int dtype, void *stream);
+
+/*
  * Workspace (bytes) that global_sink_attn needs for these sizes; 0 means it
  * needs none (the workspace pointer may then be NULL).  The value does not
  * depend on dtype.

@@ -20,6 +20,8 @@ from ._lib import SwaError
 __all__ = [
     "swa_sink_prefill",
     "swa_sink_decode",
+    "swa_sink_decode_ring",
+    "swa_sink_rope_append",
     "global_sink_attn",
     "global_sink_attn_workspace_bytes",
     "global_sink_attn_block_max",
@@ -115,6 +117,55 @@ def swa_sink_decode(q, kcache, vcache, sink, cache_len=None, out=None, lse=None,
           _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, T, W, D, _ptr(cache_len), dt,
           _stream(stream))
     return out, lse
+
+
+def swa_sink_decode_ring(q, kcache, vcache, sink, window: int, cache_len=None, out=None, lse=None,
+                         want_lse: bool = True, stream=None):
+    """Ring decode with an attention window of ``window`` keys in a ring of
+    R = kcache.shape[2] >= window slots (R >= window + T_q - 1 gives every
+    draft its full window under rollback).  Query t at position
+    p = L - T_q + t sees max(0, L - R, p - window + 1) .. p.
+    Returns (out, lse [B, Hq, T_q])."""
+    B, T, Hq, D = q.shape
+    Bk, Hkv, R, Dk = kcache.shape
+    if Bk != B or Dk != D or vcache.shape != kcache.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch")
+    if cache_len is not None and (cache_len.dtype != torch.int32 or cache_len.shape != (B,)):
+        raise ValueError("cache_len must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), device=q.device, dtype=torch.float32)
+    _check_device(q, kcache, vcache, sink, out, lse, cache_len)
+    dt = _dtype_code(q, kcache, vcache, out)
+    _call(_lib.load().swa_sink_decode_ring, "swa_sink_decode_ring", _ptr(q), _ptr(kcache),
+          _ptr(vcache), _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, T, int(window), R, D,
+          _ptr(cache_len), dt, _stream(stream))
+    return out, lse
+
+
+def swa_sink_rope_append(q, k_new, v_new, kcache, vcache, cache_len_old=None, rope_theta=10000.0,
+                         q_rot=None, stream=None):
+    """RoPE on the T_q new queries and keys at positions cache_len_old + t and
+    the rotated keys and the values written to ring slots (position mod R) of
+    kcache / vcache [B, Hkv, R, D] in place.  Returns q_rot [B, T_q, Hq, D]
+    (``q_rot=q`` rotates in place)."""
+    B, T, Hq, D = q.shape
+    Bk, Hkv, R, Dk = kcache.shape
+    if (k_new.shape != (B, T, Hkv, D) or v_new.shape != k_new.shape or Bk != B or Dk != D
+            or vcache.shape != kcache.shape):
+        raise ValueError("shape mismatch")
+    if cache_len_old is not None and (cache_len_old.dtype != torch.int32
+                                      or cache_len_old.shape != (B,)):
+        raise ValueError("cache_len_old must be int32 [B]")
+    if q_rot is None:
+        q_rot = torch.empty_like(q)
+    _check_device(q, k_new, v_new, kcache, vcache, q_rot, cache_len_old)
+    dt = _dtype_code(q, k_new, v_new, kcache, vcache, q_rot)
+    _call(_lib.load().swa_sink_rope_append, "swa_sink_rope_append", _ptr(q), _ptr(k_new),
+          _ptr(v_new), _ptr(q_rot), _ptr(kcache), _ptr(vcache), _ptr(cache_len_old), B, Hq, Hkv,
+          T, R, D, float(rope_theta), dt, _stream(stream))
+    return q_rot
 
 
 def global_sink_attn_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D) -> int:

@@ -17,6 +17,8 @@ SWA_ERR_NULL, SWA_ERR_SHAPE, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP
 EXPORTS = (
     "swa_sink_prefill",
     "swa_sink_decode",
+    "swa_sink_decode_ring",
+    "swa_sink_rope_append",
     "global_sink_attn_workspace_bytes",
     "global_sink_attn",
     "global_sink_attn_block_max",
@@ -56,6 +58,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.global_sink_attn_block_max.argtypes = [vp, vp, vp, fp, vp, fp, fp, i, i, i, i, i, i, i,
                                                i, vp]
     lib.global_sink_attn_block_max.restype = i
+    lib.swa_sink_decode_ring.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp, i, vp]
+    lib.swa_sink_decode_ring.restype = i
+    lib.swa_sink_rope_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                         ctypes.c_double, i, vp]
+    lib.swa_sink_rope_append.restype = i
     lib.swa_sink_backward_workspace_bytes.argtypes = [i, i, i]
     lib.swa_sink_backward_workspace_bytes.restype = sz
     lib.swa_sink_backward.argtypes = [vp, vp, vp, fp, vp, fp, vp, vp, vp, vp, fp,

@@ -3,6 +3,8 @@
 // launchers, and status codes.
 #include "swa_sink.h"
 
+#include <cmath>
+
 #include "launch.h"
 
 namespace {
@@ -68,10 +70,52 @@ int swa_sink_decode(const void *q, const void *kcache, const void *vcache, const
     if (!grid_fits((long)B * Hq * T_q)) return SWA_ERR_SHAPE;
     if ((long)window * D * 2 > kMaxGridX) return SWA_ERR_UNSUPPORTED;   // one ring's buffer window
 
-    swa::DecodeArgs a{q, kcache, vcache, sink, out, lse, cache_len, B, Hq, Hkv, T_q, window, D};
+    swa::DecodeArgs a{q, kcache, vcache, sink, out, lse, cache_len, B, Hq, Hkv, T_q, window, D,
+                      window};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_ring(a, st));
     return status_of(swa::launch_ring_decode_bf16(a, st));
+}
+
+int swa_sink_decode_ring(const void *q, const void *kcache, const void *vcache, const float *sink,
+                         void *out, float *lse, int B, int Hq, int Hkv, int T_q, int window,
+                         int ring, int D, const int32_t *cache_len, int dtype, void *stream) {
+    if (!q || !kcache || !vcache || !sink || !out) return SWA_ERR_NULL;
+    if (T_q < 0 || window < 1 || ring < window || T_q > ring) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4) || !aligned(cache_len, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || T_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hq * T_q)) return SWA_ERR_SHAPE;
+    if ((long)ring * D * 2 > kMaxGridX) return SWA_ERR_UNSUPPORTED;     // one ring's buffer window
+
+    swa::DecodeArgs a{q, kcache, vcache, sink, out, lse, cache_len, B, Hq, Hkv, T_q, window, D,
+                      ring};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_ring(a, st));
+    return status_of(swa::launch_ring_decode_bf16(a, st));
+}
+
+int swa_sink_rope_append(const void *q, const void *k_new, const void *v_new, void *q_rot,
+                         void *kcache, void *vcache, const int32_t *cache_len_old, int B, int Hq,
+                         int Hkv, int T_q, int ring, int D, double rope_theta, int dtype,
+                         void *stream) {
+    if (!q || !k_new || !v_new || !q_rot || !kcache || !vcache) return SWA_ERR_NULL;
+    if (T_q < 0 || ring < 1 || T_q > ring) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return SWA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_rot, 16) ||
+        !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(cache_len_old, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || T_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * T_q)) return SWA_ERR_SHAPE;
+
+    swa::AppendArgs a{q, k_new, v_new, q_rot, kcache, vcache, cache_len_old,
+                      B, Hq, Hkv, T_q, ring, D, rope_theta};
+    return status_of(swa::launch_rope_append(a, dtype == SWA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 size_t global_sink_attn_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {

@@ -29,7 +29,8 @@ constexpr int kWavesPerWG = 4;      // independent waves per work-group
 
 // Mode RING: keys are ring slots 0..W-1 of [B, Hkv, W, D]; with base =
 // (L-1) mod W the slot j holds position L-1-base+j, minus W when j > base,
-// visible to token t when it lies in [max(0, L-W), L-T+t].  Mode LINEAR:
+// visible to token t when it lies in [max(0, L-W, p-Wnd+1), p], p = L-T+t
+// (Wnd: the attention window, at most the W slots).  Mode LINEAR:
 // keys are positions [k_begin, k_end) of [B, S_kv, Hkv, D] (one split),
 // visible to token t when <= S_kv-T+t.
 //
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ kc, const bf16 *__restrict__ vc,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse,
     const int32_t *__restrict__ cache_len, int B, int Hq, int Hkv, int T, int W, int S_kv,
-    int kps, int n_ct, int n_splits, float *__restrict__ part) {
+    int kps, int n_ct, int n_splits, float *__restrict__ part, int Wnd) {
     constexpr int KF = D / 16;                     // Q fragments, K loads per lane
     constexpr int VPT = D / 64;                    // V items (4 keys x 8 dims) per lane
     constexpr float kSlack = 8.0f;                 // log2 units
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
         const int L = cache_len ? cache_len[b] : W;
         wrap_base = (L - 1) % W;                             // slot of the newest token
         pos0 = L - 1 - wrap_base;                            // position of slot 0 (before wrap)
-        lo = max(0, L - W);
         hi = L - T + t;
+        lo = max(max(0, L - W), hi - Wnd + 1);               // in the ring and in the window
         n_keys = W;
         rs = (uint32_t)D * 2;
         kbase = kc + ((size_t)b * Hkv + g) * (size_t)W * D;
@@ -325,8 +326,8 @@ hipError_t ring_decode_d(const DecodeArgs &a, hipStream_t stream) {
     const long items = (long)n_ct * a.Hkv * a.B;
     hipLaunchKernelGGL((decode_kernel<D, true>), dim3(waves_to_groups(items)), dim3(64 * kWavesPerWG),
                        0, stream, (const bf16 *)a.q, (const bf16 *)a.kcache, (const bf16 *)a.vcache,
-                       a.sink, (bf16 *)a.out, a.lse, a.cache_len, a.B, a.Hq, a.Hkv, a.T, a.W, 0, 0,
-                       n_ct, 1, (float *)nullptr);
+                       a.sink, (bf16 *)a.out, a.lse, a.cache_len, a.B, a.Hq, a.Hkv, a.T, a.R, 0, 0,
+                       n_ct, 1, (float *)nullptr, a.W);
     return hipGetLastError();
 }
 
@@ -363,7 +364,7 @@ hipError_t splitkv_d(const PrefillArgs &a, void *workspace, hipStream_t stream) 
                        dim3(64 * kWavesPerWG), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
                        (const bf16 *)a.v, a.sink, (bf16 *)nullptr, (float *)nullptr,
                        (const int32_t *)nullptr, a.B, a.Hq, a.Hkv, a.S, 0, a.S_kv, p.kps, p.n_ct,
-                       p.n_splits, part);
+                       p.n_splits, part, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((combine_kernel<D>), dim3(a.B * a.Hq * a.S), dim3(64), 0, stream, part,

@@ -35,10 +35,11 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     __syncthreads();
 
     long lo, hi;
-    if (RING) {   // nkeys == window == ring slots; positions max(0, L-W) .. L-T+row
-        const long L = cache_len ? (long)cache_len[b] : (long)window;
+    if (RING) {   // nkeys = ring slots; positions max(0, L-nkeys, p-window+1) .. p = L-T+row
+        const long L = cache_len ? (long)cache_len[b] : (long)nkeys;
         hi = L - rows + row;
-        lo = L - window > 0 ? L - window : 0;
+        lo = L - nkeys > 0 ? L - nkeys : 0;
+        lo = hi - window + 1 > lo ? hi - window + 1 : lo;
     } else {      // rows aligned to the end of the keys
         hi = (long)nkeys - rows + row;
         lo = hi - window + 1 > 0 ? hi - window + 1 : 0;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     for (long j = lo + lane; j <= hi; j += 64) {
         size_t off;
         if (RING)
-            off = (((size_t)b * Hkv + g) * window + (size_t)(j % window)) * D;
+            off = (((size_t)b * Hkv + g) * nkeys + (size_t)(j % nkeys)) * D;
         else
             off = (((size_t)b * nkeys + j) * Hkv + g) * D;
         const float *kr = k + off;
@@ -115,7 +116,7 @@ hipError_t ring_d(const DecodeArgs &a, hipStream_t stream) {
     dim3 grid(a.T, a.Hq, a.B);
     hipLaunchKernelGGL((generic_f32_kernel<D, true>), grid, dim3(64), 0, stream,
                        (const float *)a.q, (const float *)a.kcache, (const float *)a.vcache,
-                       a.sink, (float *)a.out, a.lse, a.Hq, a.Hkv, a.T, a.W, a.W, a.cache_len);
+                       a.sink, (float *)a.out, a.lse, a.Hq, a.Hkv, a.T, a.R, a.W, a.cache_len);
     return hipGetLastError();
 }
 

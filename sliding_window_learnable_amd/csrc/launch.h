@@ -25,9 +25,21 @@ struct DecodeArgs {
     const float *sink;
     void *out;
     float *lse;
-    const int32_t *cache_len;   // may be NULL: L = window
-    int B, Hq, Hkv, T, W, D;
+    const int32_t *cache_len;   // may be NULL: L = R (every ring full)
+    int B, Hq, Hkv, T, W, D;    // W: keys per query (window)
+    int R;                      // ring slots (>= W)
 };
+
+// RoPE on the T new queries and keys at positions L_old + t, keys and
+// values written to ring slots (L_old + t) mod R.
+struct AppendArgs {
+    const void *q, *k_new, *v_new;
+    void *q_rot, *kcache, *vcache;
+    const int32_t *cache_len_old;   // may be NULL: L_old = 0
+    int B, Hq, Hkv, T, R, D;
+    double theta;
+};
+hipError_t launch_rope_append(const AppendArgs &a, bool bf16, hipStream_t stream);
 
 // bf16 sliding-window prefill, LDS ring of key tiles (98 <= window <= 129).
 bool prefill_ring_supported(int window, int G);

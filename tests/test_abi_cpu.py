@@ -206,3 +206,45 @@ def test_block_max_rejects(lib, kw, code):
 def test_block_max_empty_is_noop(lib):
     assert bmax(lib, B=0) == _lib.SWA_OK
     assert bmax(lib, Sq=0) == _lib.SWA_OK
+
+
+def dring(lib, q=P, kc=P, vc=P, sink=P, out=P, lse=None, B=1, Hq=8, Hkv=1, T=4, W=128, R=131,
+          D=128, cache_len=None, dtype=1):
+    return lib.swa_sink_decode_ring(q, kc, vc, sink, out, lse, B, Hq, Hkv, T, W, R, D, cache_len,
+                                    dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(W=0), _lib.SWA_ERR_SHAPE), (dict(R=100), _lib.SWA_ERR_SHAPE),
+    (dict(T=132), _lib.SWA_ERR_SHAPE), (dict(T=-1), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE),
+    (dict(D=80), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=4), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(cache_len=P + 2), _lib.SWA_ERR_UNSUPPORTED), (dict(kc=P + 8), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_decode_ring_rejects(lib, kw, code):
+    assert dring(lib, **kw) == code
+
+
+def rapp(lib, q=P, kn=P, vn=P, qr=P, kc=P, vc=P, cl=None, B=1, Hq=8, Hkv=1, T=4, R=131, D=128,
+         theta=10000.0, dtype=1):
+    return lib.swa_sink_rope_append(q, kn, vn, qr, kc, vc, cl, B, Hq, Hkv, T, R, D, theta, dtype,
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(qr=None), _lib.SWA_ERR_NULL),
+    (dict(kc=None), _lib.SWA_ERR_NULL),
+    (dict(T=132), _lib.SWA_ERR_SHAPE), (dict(R=0), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), _lib.SWA_ERR_SHAPE),
+    (dict(theta=1.0), _lib.SWA_ERR_UNSUPPORTED), (dict(theta=float("nan")), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=2), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(vn=P + 8), _lib.SWA_ERR_UNSUPPORTED), (dict(cl=P + 1), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_rope_append_rejects(lib, kw, code):
+    assert rapp(lib, **kw) == code
+
+
+def test_ring_calls_empty_are_noops(lib):
+    assert dring(lib, B=0) == _lib.SWA_OK and dring(lib, T=0) == _lib.SWA_OK
+    assert rapp(lib, B=0) == _lib.SWA_OK and rapp(lib, T=0) == _lib.SWA_OK
