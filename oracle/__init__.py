@@ -14,6 +14,7 @@ numpy arrays into contiguous float64 buffers, and states each call's key set:
 * global causal attention -- with S_q queries at the end of S_kv keys, row i
   sits at position S_kv - S_q + i and sees 0 .. that position (same digest,
   混合注意力机制: global layers see the whole sequence);
+* packed batches of sequences of different lengths -- see ``prefill_varlen``;
 * ring decode -- see ``ring_decode``;
 * the gradients of the first two -- see ``attend_backward``;
 * block maxima of the global layer's logits -- see ``block_max``.
@@ -139,6 +140,31 @@ def swa_prefill(q, k, v, sink, window):
     rp = np.tile(np.arange(S), B)
     out, lse = swa_prefill_rows(q.reshape(B * S, Hq, D), rb, rp, k, v, sink, window)
     return out.reshape(B, S, Hq, D), lse.reshape(B, S, Hq).transpose(0, 2, 1).copy()
+
+
+def prefill_varlen(q, k, v, sink, cu_seqlens, window):
+    """Packed batch of sequences of different lengths: sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [total, Hq, D] and k/v
+    [total, Hkv, D], and is a causal window-``window`` prefill on its own
+    (positions restart at 0 per sequence; no row sees another sequence).
+    Serving mixed context lengths together: "小米罗福莉：MiMo-V2.5如何做到
+    又快又强又便宜？| ICML 2026", §06 Q&A, audience E.
+
+    -> out [total, Hq, D], lse [Hq, total] (float64).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    total, Hq, D = q.shape
+    assert cu[0] == 0 and cu[-1] == total and all(a <= b for a, b in zip(cu, cu[1:]))
+    out = np.zeros((total, Hq, D), dtype=np.float64)
+    lse = np.zeros((Hq, total), dtype=np.float64)
+    for s0, s1 in zip(cu, cu[1:]):
+        if s1 == s0:
+            continue
+        o, l = swa_prefill(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], sink, window)
+        out[s0:s1] = o[0]
+        lse[:, s0:s1] = l[0]
+    return out, lse
 
 
 def global_rows(q_rows, row_batch, row_pos, k, v, sink):
