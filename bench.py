@@ -13,6 +13,8 @@ same JSON object:
   long_context  SWA prefill at S=262144; global decode B=8 over 262144 keys
   backward      swa_sink_backward (dq, dk, dv, dsink) at the 32K SWA workload
                 and on a 16K global layer, with the forward time beside it
+  varlen        packed prefill of 16 sequences of mixed length (one context
+                bucket), window 128 and global, against the padded batch
 Inputs are seeded synthetic Gaussian tensors resident in HBM before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTION]
@@ -48,7 +50,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "decode", "hybrid", "long", "backward", "copy"])
+                    choices=["all", "prefill", "decode", "hybrid", "long", "backward", "varlen",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -347,6 +350,58 @@ def bench_backward(args, swa, acc, torch):
     return res
 
 
+def bench_varlen(args, swa, acc, torch):
+    """swa_sink_prefill_varlen on one context-length bucket: 16 sequences with
+    lengths uniform in [512, 8192], packed, as a window-128 layer and as a
+    global causal layer; against the same batch padded to the longest length
+    and run through the uniform-batch entry points."""
+    from sliding_window_learnable_amd import inputs
+    Hq, Hkv, D, W = 64, 8, 128, 128
+    lengths = [int(n) for n in inputs.cache_lengths(16, 512, 8192, seed=6000)]
+    S_max, total = max(lengths), sum(lengths)
+    res = {"workload": "packed bf16 batch of 16 sequences, lengths uniform in [512, 8192] "
+                       "(seed 6000; %d tokens, longest %d), Hq=64 Hkv=8 D=128" % (total, S_max),
+           "lengths": lengths}
+    q, k, v, sink, cu = inputs.packed_inputs(6, 0, lengths, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, total), device="cuda", dtype=torch.float32)
+    B = len(lengths)
+    for name, win, steps in (("swa_window_128", W, 100), ("global_causal", S_max, 10)):
+        log("varlen %s: %d steps" % (name, steps))
+        ms = timed(lambda i: swa.swa_sink_prefill_varlen(q, k, v, sink, cu, S_max, win, out=out,
+                                                         lse=lse), steps, max(3, steps // 5))
+        pairs = sum(acc.window_pairs(n, win) for n in lengths)
+        fl = 4 * D * Hq * pairs
+        nb = acc.prefill_bytes(1, total, Hq, Hkv, D)
+        res[name] = dict(ms=ms, tokens_per_s=total / (ms * 1e-3),
+                         tflops=fl / (ms * 1e-3) / 1e12,
+                         frac_mfma_peak=fl / (ms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
+                         hbm_gbs=nb / (ms * 1e-3) / 1e9,
+                         frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS)
+    del out, lse
+    # the same sequences padded on the right to S_max, as a [B, S_max] batch
+    qp = torch.zeros((B, S_max, Hq, D), device="cuda", dtype=torch.bfloat16)
+    kp = torch.zeros((B, S_max, Hkv, D), device="cuda", dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    offs = [0]
+    for n in lengths:
+        offs.append(offs[-1] + n)
+    for b, n in enumerate(lengths):
+        qp[b, :n], kp[b, :n], vp[b, :n] = q[offs[b]:offs[b + 1]], k[offs[b]:offs[b + 1]], \
+            v[offs[b]:offs[b + 1]]
+    del q, k, v
+    outp = torch.empty_like(qp)
+    lsep = torch.empty((B, Hq, S_max), device="cuda", dtype=torch.float32)
+    log("varlen: padded batch, window 128 and global")
+    ms_w = timed(lambda i: swa.swa_sink_prefill(qp, kp, vp, sink, W, out=outp, lse=lsep), 100, 20)
+    ms_g = timed(lambda i: swa.global_sink_attn(qp, kp, vp, sink, out=outp, lse=lsep), 10, 3)
+    res["swa_window_128"]["padded_batch_ms"] = ms_w
+    res["global_causal"]["padded_batch_ms"] = ms_g
+    del qp, kp, vp, outp, lsep, sink, cu
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy(args, torch):
     """Plain 1 GiB device copy: the reference kernel for scaling PMC byte counters."""
     n = 1 << 30
@@ -419,6 +474,8 @@ def main():
         result["long_context"] = bench_long(args, swa, acc, torch)
     if args.only in ("all", "backward"):
         result["backward"] = bench_backward(args, swa, acc, torch)
+    if args.only in ("all", "varlen"):
+        result["varlen"] = bench_varlen(args, swa, acc, torch)
     print(json.dumps(result))
 
 

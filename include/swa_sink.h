@@ -89,6 +89,33 @@ SWA_API int swa_sink_prefill(const void *q, const void *k, const void *v, const 
                      int window, int dtype, void *stream);
 
 /*
+ * swa_sink_prefill over a packed batch of sequences of different lengths
+ * (context-length buckets served together).  Source: "小米罗福莉：MiMo-V2.5
+ * 如何做到又快又强又便宜？| ICML 2026", §06 Q&A (audience E: requests are
+ * grouped into buckets by context length); the attention itself is that of
+ * swa_sink_prefill, applied to each sequence on its own.
+ *
+ *   q, out  [total, Hq, D]    k, v [total, Hkv, D]    sink [Hq] (float32)
+ *   lse     [Hq, total] (float32, natural log; may be NULL)
+ *   cu_seqlens  int32 [B + 1] on the device: sequence b is rows
+ *               cu_seqlens[b] .. cu_seqlens[b+1] - 1; cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[B] = total, every length
+ *               <= max_seqlen.  The kernels clamp each entry to that range,
+ *               so a malformed table gives wrong rows but no access outside
+ *               the tensors.
+ * Row i of a sequence sees its own rows max(0, i - window + 1) .. i; window
+ * >= max_seqlen gives causal global attention per sequence.  Zero-length
+ * sequences are allowed.  Work-groups for rows past a sequence's end exit at
+ * once, so the cost follows max_seqlen * B for the launch and the real rows
+ * for the arithmetic.
+ */
+SWA_API int swa_sink_prefill_varlen(const void *q, const void *k, const void *v,
+                                    const float *sink, void *out, float *lse,
+                                    const int32_t *cu_seqlens, int B, int max_seqlen,
+                                    int total, int Hq, int Hkv, int D, int window,
+                                    int dtype, void *stream);
+
+/*
  * Decode over a fixed ring KV cache of `window` slots per (sequence, KV head),
  * with T_q >= 1 new query tokens per sequence (T_q > 1 verifies MTP draft
  * tokens in one pass).  Sources: pwwt.cn article, §1.1 Hybrid Attention

@@ -19,6 +19,7 @@ from ._lib import SwaError
 
 __all__ = [
     "swa_sink_prefill",
+    "swa_sink_prefill_varlen",
     "swa_sink_decode",
     "swa_sink_decode_ring",
     "swa_sink_rope_append",
@@ -90,6 +91,36 @@ def swa_sink_prefill(q, k, v, sink, window: int, out=None, lse=None, want_lse: b
     dt = _dtype_code(q, k, v, out)
     _call(_lib.load().swa_sink_prefill, "swa_sink_prefill", _ptr(q), _ptr(k), _ptr(v),
           _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, int(window), dt, _stream(stream))
+    return out, lse
+
+
+def swa_sink_prefill_varlen(q, k, v, sink, cu_seqlens, max_seqlen: int, window: int, out=None,
+                            lse=None, want_lse: bool = True, stream=None):
+    """Sliding-window (or, with window >= max_seqlen, global causal) prefill
+    over a packed batch: q [total, Hq, D], k/v [total, Hkv, D], cu_seqlens
+    int32 [B + 1] on the GPU (sequence b is rows cu_seqlens[b] ..
+    cu_seqlens[b+1] - 1, each at most max_seqlen long).
+    Returns (out [total, Hq, D], lse [Hq, total] float32 or None).
+    """
+    total, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (total, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch: q %s k %s v %s sink %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(sink.shape)))
+    if sink.dtype != torch.float32:
+        raise TypeError("sink must be float32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be int32 [B + 1]")
+    B = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, total), device=q.device, dtype=torch.float32)
+    _check_device(q, k, v, sink, out, lse, cu_seqlens)
+    dt = _dtype_code(q, k, v, out)
+    _call(_lib.load().swa_sink_prefill_varlen, "swa_sink_prefill_varlen", _ptr(q), _ptr(k),
+          _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), _ptr(cu_seqlens), B, int(max_seqlen),
+          total, Hq, Hkv, D, int(window), dt, _stream(stream))
     return out, lse
 
 

@@ -16,6 +16,7 @@ SWA_ERR_NULL, SWA_ERR_SHAPE, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP
 
 EXPORTS = (
     "swa_sink_prefill",
+    "swa_sink_prefill_varlen",
     "swa_sink_decode",
     "swa_sink_decode_ring",
     "swa_sink_rope_append",
@@ -49,6 +50,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.swa_sink_prefill.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp]
     lib.swa_sink_prefill.restype = i
+    lib.swa_sink_prefill_varlen.argtypes = [vp, vp, vp, fp, vp, fp, vp, i, i, i, i, i, i, i, i,
+                                            vp]
+    lib.swa_sink_prefill_varlen.restype = i
     lib.swa_sink_decode.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, i, vp]
     lib.swa_sink_decode.restype = i
     lib.global_sink_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]

@@ -56,6 +56,29 @@ int swa_sink_prefill(const void *q, const void *k, const void *v, const float *s
     return status_of(swa::launch_stream_bf16(a, st));
 }
 
+int swa_sink_prefill_varlen(const void *q, const void *k, const void *v, const float *sink,
+                            void *out, float *lse, const int32_t *cu_seqlens, int B,
+                            int max_seqlen, int total, int Hq, int Hkv, int D, int window,
+                            int dtype, void *stream) {
+    if (!q || !k || !v || !sink || !out || !cu_seqlens) return SWA_ERR_NULL;
+    if (max_seqlen < 0 || total < 0 || window < 1) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4) || !aligned(cu_seqlens, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || max_seqlen == 0 || total == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hkv * ((max_seqlen + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+
+    swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, max_seqlen, max_seqlen, D,
+                       window, cu_seqlens, total};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_linear(a, st));
+    if (swa::prefill_ring_supported(window, Hq / Hkv))
+        return status_of(swa::launch_prefill_ring_bf16(a, st));
+    return status_of(swa::launch_stream_bf16(a, st));
+}
+
 int swa_sink_decode(const void *q, const void *kcache, const void *vcache, const float *sink,
                     void *out, float *lse, int B, int Hq, int Hkv, int T_q, int window, int D,
                     const int32_t *cache_len, int dtype, void *stream) {

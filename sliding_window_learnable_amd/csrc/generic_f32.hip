@@ -20,7 +20,8 @@ template <int D, bool RING>
 __global__ __launch_bounds__(64) void generic_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ sink, float *__restrict__ out, float *__restrict__ lse,
-    int Hq, int Hkv, int rows, int nkeys, int window, const int32_t *__restrict__ cache_len) {
+    int Hq, int Hkv, int rows, int nkeys, int window, const int32_t *__restrict__ cache_len,
+    const int32_t *__restrict__ cu, int total) {
     __shared__ float qs[D];
     __shared__ float red[64][D + 1];
     __shared__ float wts[64];
@@ -30,7 +31,17 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     const int g = h / (Hq / Hkv);
     const float c = kLog2e / sqrtf((float)D);
 
-    const size_t qoff = (((size_t)b * rows + row) * Hq + h) * D;
+    // Packed variable-length batch (linear mode, cu != nullptr): sequence b
+    // is rows cu[b] .. cu[b+1]-1 of [total, H, D]; lse is [Hq, total].
+    size_t q_row0 = (size_t)b * rows, kv_row0 = (size_t)b * nkeys;
+    if (!RING && cu != nullptr) {
+        const int s0 = min(max(cu[b], 0), total);   // clamped against a malformed table
+        const int s1 = min(max(cu[b + 1], s0), min(total, s0 + rows));
+        rows = nkeys = s1 - s0;
+        q_row0 = kv_row0 = (size_t)s0;
+        if (row >= rows) return;                       // whole work-group, before any barrier
+    }
+    const size_t qoff = ((q_row0 + row) * Hq + h) * D;
     for (int d = lane; d < D; d += 64) qs[d] = q[qoff + d];
     __syncthreads();
 
@@ -54,7 +65,7 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
         if (RING)
             off = (((size_t)b * Hkv + g) * nkeys + (size_t)(j % nkeys)) * D;
         else
-            off = (((size_t)b * nkeys + j) * Hkv + g) * D;
+            off = ((kv_row0 + j) * Hkv + g) * D;
         const float *kr = k + off;
         const float *vr = v + off;
         float x = 0.0f;
@@ -97,7 +108,7 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
         out[qoff + d] = s * inv;
     }
     if (lse != nullptr && lane == 0)
-        lse[((size_t)b * Hq + h) * rows + row] =
+        lse[(!RING && cu != nullptr ? (size_t)h * total + q_row0 : ((size_t)b * Hq + h) * rows) + row] =
             Ltot > 0.0f ? (Mu + log2f(Ltot)) * kLn2 : -INFINITY;
 }
 
@@ -107,7 +118,7 @@ hipError_t linear_d(const PrefillArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((generic_f32_kernel<D, false>), grid, dim3(64), 0, stream,
                        (const float *)a.q, (const float *)a.k, (const float *)a.v, a.sink,
                        (float *)a.out, a.lse, a.Hq, a.Hkv, a.S, a.S_kv, a.window,
-                       (const int32_t *)nullptr);
+                       (const int32_t *)nullptr, a.cu_seqlens, a.total);
     return hipGetLastError();
 }
 
@@ -116,7 +127,8 @@ hipError_t ring_d(const DecodeArgs &a, hipStream_t stream) {
     dim3 grid(a.T, a.Hq, a.B);
     hipLaunchKernelGGL((generic_f32_kernel<D, true>), grid, dim3(64), 0, stream,
                        (const float *)a.q, (const float *)a.kcache, (const float *)a.vcache,
-                       a.sink, (float *)a.out, a.lse, a.Hq, a.Hkv, a.T, a.R, a.W, a.cache_len);
+                       a.sink, (float *)a.out, a.lse, a.Hq, a.Hkv, a.T, a.R, a.W, a.cache_len,
+                       (const int32_t *)nullptr, 0);
     return hipGetLastError();
 }
 

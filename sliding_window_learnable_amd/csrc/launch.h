@@ -18,6 +18,8 @@ struct PrefillArgs {            // also used for global attention
     int S_kv;                   // key rows per sequence
     int D;
     int window;                 // keys per row, counting the row itself
+    const int32_t *cu_seqlens = nullptr;   // packed varlen batch: [B+1] row offsets (S = max length)
+    int total = 0;              // rows of the packed batch
 };
 
 struct DecodeArgs {

@@ -51,8 +51,9 @@ struct StreamSmem {
 template <int D, int NW, bool BLK>
 __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S_q,
-    int S_kv, int Hq, int Hkv, int W, int BG, int NB, float *__restrict__ bmax, int rk, int NKB) {
+    const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S_q_,
+    int S_kv_, int Hq, int Hkv, int W, int BG, int NB, float *__restrict__ bmax, int rk, int NKB,
+    const int32_t *__restrict__ cu, int total) {
     __shared__ __align__(16) StreamSmem<D> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -64,7 +65,19 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const int G = Hq / Hkv;
     const float c = kLog2e / sqrtf((float)D);
 
+    // Packed variable-length batch (cu != nullptr): sequence b owns rows
+    // cu[b] .. cu[b+1]-1 of [total, H, D] tensors (lse [Hq, total]) and
+    // attends within itself; otherwise [B, S, H, D] (lse [B, Hq, S_q]).
+    int S_q = S_q_, S_kv = S_kv_;
+    size_t q_row0 = (size_t)b * S_q_, kv_row0 = (size_t)b * S_kv_;
+    if (cu != nullptr) {   // clamped so a malformed table cannot index past the tensors
+        const int s0 = min(max(cu[b], 0), total);
+        const int s1 = min(max(cu[b + 1], s0), min(total, s0 + S_q_));
+        S_q = S_kv = s1 - s0;
+        q_row0 = kv_row0 = (size_t)s0;
+    }
     const int i0 = qb * kTile;                         // first query row of the block
+    if (i0 >= S_q) return;                             // past this sequence (uniform, before any barrier)
     const int off = S_kv - S_q;                        // row i sits at position off + i
     const int p_first = off + i0;
     const int p_last = off + min(S_q - 1, i0 + kTile - 1);
@@ -74,8 +87,8 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 
     const size_t row_elems = (size_t)Hkv * D;
     const uint32_t rs = (uint32_t)row_elems * 2;
-    const bf16 *kb = k + ((size_t)b * S_kv * Hkv + g) * D;
-    const bf16 *vb = v + ((size_t)b * S_kv * Hkv + g) * D;
+    const bf16 *kb = k + (kv_row0 * Hkv + g) * D;
+    const bf16 *vb = v + (kv_row0 * Hkv + g) * D;
 
     const int i = i0 + lq;                             // this lane's query row
     const bool row_ok = i < S_q;
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         if (hh != wave) lds_barrier();                 // previous head's reads are done
         bf16x8 qf[D / 16];
         {
-            const bf16 *qrow = q + (((size_t)b * S_q + min(i, S_q - 1)) * Hq + h) * D + 8 * hl;
+            const bf16 *qrow = q + ((q_row0 + min(i, S_q - 1)) * Hq + h) * D + 8 * hl;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 #pragma unroll
@@ -279,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         const float lt = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
         if (row_ok) {
             const float inv = lt > 0.0f ? __builtin_amdgcn_rcpf(lt) : 0.0f;
-            bf16 *orow = out + (((size_t)b * S_q + i) * Hq + h) * D;
+            bf16 *orow = out + ((q_row0 + i) * Hq + h) * D;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
                 }
             }
             if (lse != nullptr && hl == 0)
-                lse[((size_t)b * Hq + h) * S_q + i] =
+                lse[(cu != nullptr ? (size_t)h * total + q_row0 : ((size_t)b * Hq + h) * S_q) + i] =
                     lt > 0.0f ? (mu + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
         }
     }
@@ -306,7 +319,7 @@ hipError_t launch(const PrefillArgs &a, float *bmax, int block_k, hipStream_t st
     hipLaunchKernelGGL((stream_attn_kernel<D, NW, BLK>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
                        stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
                        (bf16 *)a.out, a.lse, a.S, a.S_kv, a.Hq, a.Hkv, a.window, BG, NB, bmax, rk,
-                       NKB);
+                       NKB, a.cu_seqlens, a.total);
     return hipGetLastError();
 }
 

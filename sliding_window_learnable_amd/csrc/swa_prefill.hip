@@ -109,11 +109,12 @@ struct Stager {
 // ring slot at its end, and output stores are never waited on.  Every
 // global access is a buffer access relative to this work-group's window of
 // the tensor, so rows past the end need no special code.
-template <int D, int NW>
+template <int D, int NW, bool PACKED>
 __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S,
-    int Hq, int Hkv, int W, int ntw, int chunk) {
+    int Hq, int Hkv, int W, int ntw, int chunk, const int32_t *__restrict__ cu, int B,
+    int total) {
     constexpr int NT = NW * 64;
     constexpr float kSlack = 8.0f;                               // log2 units
     constexpr float kBig = 256.0f;                               // 2^kSlack
@@ -122,30 +123,22 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lq = lane & 31, hl = lane >> 5;
-    const int g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.y;
     const int h = g * NW + wave;
     const int R = ntw + 1;
-    const int c0 = blockIdx.x * chunk;
-    const int c1 = min(S, c0 + chunk);
     const float c = kLog2e / sqrtf((float)D);
     // key - query for accumulator register r of a tile starting rel keys
     // after the step's first query: 16(r>>3) + (r&7) + kbias + rel
     const int kbias = 8 * hl - lq;
-
-    // Buffer windows: q/out rows [c0, c1) of this batch (all heads); k/v rows
-    // [r0, S) of KV head g; lse row of head h.
     const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
     const uint32_t rs = (uint32_t)Hkv * D * 2;
-    const int T_first = max(0, c0 / kTile - ntw + 1);
-    const int r0 = kTile * T_first;
-    const rsrc_t qr = make_rsrc(q + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
-    const rsrc_t orr = make_rsrc(out + (((size_t)b * S + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
-    // K/V rows [r0, c1): every row this chunk uses (the prefetch past the
-    // chunk's last tile reads zeros and is never stored).
-    const rsrc_t kr = make_rsrc(k + (((size_t)b * S + r0) * Hkv + g) * D, (c1 - r0) * rs);
-    const rsrc_t vr = make_rsrc(v + (((size_t)b * S + r0) * Hkv + g) * D, (c1 - r0) * rs);
-    const rsrc_t lr = make_rsrc(lse != nullptr ? lse + ((size_t)b * Hq + h) * S + c0 : nullptr,
-                                lse != nullptr ? (uint32_t)(c1 - c0) * 4 : 0u);
+
+    // The segment being computed: positions [c0, c1) of one sequence.
+    // Buffer windows: q/out rows [c0, c1) (all heads); k/v rows [r0, c1) of
+    // KV head g -- every row the segment uses (the prefetch past its last
+    // tile reads zeros and is never stored); the lse entries of head h.
+    int c0 = 0, c1 = 0, r0 = 0;
+    rsrc_t qr, orr, kr, vr, lr;
     // QK contraction order: lane half hl feeds dims [64hl, 64hl + 64), the
     // ks-th MFMA step dims 64hl + 8ks .. +8, so each lane reads one whole
     // 128-byte line of its query row (K fragments use the same order).
@@ -160,10 +153,6 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     };
 
     Stager<D, NT> st;
-    for (int T = T_first; T <= c0 / kTile; ++T) {
-        st.load(kr, vr, rs, kTile * T - r0, tid);
-        st.store(sm, T % R, tid);
-    }
 
     // S^T of one tile: 32 keys of ring slot `slot` x this wave's 32 queries.
     auto qk = [&](const bf16x8 (&cur)[D / 16], int slot) {
@@ -345,12 +334,85 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         if (p0 + kTile < c1) st.store(sm, (T1 + 1) % R, tid);
     };
 
-    bf16x8 qa[D / 16], qb[D / 16];
-    load_q(qa, c0);
-    for (int p0 = c0; p0 < c1; p0 += 2 * kTile) {
-        step(qa, qb, p0);
-        if (p0 + kTile >= c1) break;
-        step(qb, qa, p0 + kTile);
+    // Segments.  Uniform batch (!PACKED): one, the chunk [c0, c1) of
+    // sequence blockIdx.z.  Packed batch: sequence s (rows cu[s] .. cu[s+1]-1)
+    // contributes ceil(len_s / 32) tiles to one concatenated list, and this
+    // work-group owns tiles [t0, t1) of it: a segment per sequence that the
+    // range meets.  Each wave finds them with the same scan of 64 sequences
+    // at a time (a prefix sum of tile counts), so every value below is
+    // wave-uniform and all waves run the same segments.
+    const int t0 = blockIdx.x * (chunk / kTile), t1 = t0 + chunk / kTile;
+    int sb = 0, carry = 0;                 // next scan batch; tiles before it
+    uint64_t pend = 0;                     // lanes of the last batch still to run
+    int l_excl = 0, l_n = 0, l_s0 = 0, l_len = 0;
+    bool first = true;
+    for (;;) {
+        size_t row0;
+        float *lrow;
+        if constexpr (!PACKED) {
+            if (!first) break;
+            const int b = blockIdx.z;
+            row0 = (size_t)b * S;
+            c0 = blockIdx.x * chunk;
+            c1 = min(S, c0 + chunk);
+            lrow = lse != nullptr ? lse + ((size_t)b * Hq + h) * S : nullptr;
+        } else {
+            while (pend == 0 && sb < B && carry < t1) {
+                const int sq = sb + lane;
+                int s0 = 0, n_rows = 0;
+                if (sq < B) {      // clamped so a malformed table stays inside the tensors
+                    s0 = min(max(cu[sq], 0), total);
+                    n_rows = min(max(cu[sq + 1], s0), min(total, s0 + S)) - s0;
+                }
+                const int n = (n_rows + kTile - 1) / kTile;
+                int incl = n;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    incl += lane >= o ? y : 0;
+                }
+                l_excl = carry + incl - n;
+                l_n = n;
+                l_s0 = s0;
+                l_len = n_rows;
+                pend = __ballot(n > 0 && l_excl < t1 && l_excl + n > t0);
+                carry += __builtin_amdgcn_readlane(incl, 63);
+                sb += 64;
+            }
+            if (pend == 0) break;
+            const int j = __builtin_ctzll(pend);
+            pend &= pend - 1;
+            const int excl = __builtin_amdgcn_readlane(l_excl, j);
+            const int n = __builtin_amdgcn_readlane(l_n, j);
+            const int len = __builtin_amdgcn_readlane(l_len, j);
+            row0 = (size_t)__builtin_amdgcn_readlane(l_s0, j);
+            c0 = kTile * max(t0 - excl, 0);
+            c1 = min(kTile * min(t1 - excl, n), len);
+            lrow = lse != nullptr ? lse + (size_t)h * total + row0 : nullptr;
+            if (!first) __syncthreads();   // the previous segment's last reads of the ring
+        }
+        first = false;
+
+        const int T_first = max(0, c0 / kTile - ntw + 1);
+        r0 = kTile * T_first;
+        qr = make_rsrc(q + ((row0 + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
+        orr = make_rsrc(out + ((row0 + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
+        kr = make_rsrc(k + ((row0 + r0) * Hkv + g) * D, (c1 - r0) * rs);
+        vr = make_rsrc(v + ((row0 + r0) * Hkv + g) * D, (c1 - r0) * rs);
+        lr = make_rsrc(lrow != nullptr ? lrow + c0 : nullptr,
+                       lrow != nullptr ? (uint32_t)(c1 - c0) * 4 : 0u);
+        for (int T = T_first; T <= c0 / kTile; ++T) {
+            st.load(kr, vr, rs, kTile * T - r0, tid);
+            st.store(sm, T % R, tid);
+        }
+
+        bf16x8 qa[D / 16], qb[D / 16];
+        load_q(qa, c0);
+        for (int p0 = c0; p0 < c1; p0 += 2 * kTile) {
+            step(qa, qb, p0);
+            if (p0 + kTile >= c1) break;
+            step(qb, qa, p0 + kTile);
+        }
     }
 }
 
@@ -371,6 +433,24 @@ namespace {
 
 template <int D, int NW>
 hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
+    const int ntw = (a.window - 1 + kTile - 1) / kTile + 1;
+    const int cap_tiles = prefill_chunk_cap(a.Hq, a.Hkv, a.D, ntw) / kTile;
+    if (a.cu_seqlens != nullptr) {
+        // Packed batch: at most (total + 31 B) / 32 tiles in all; split them
+        // evenly over about 256 work-groups (one per CU), at least 4 tiles
+        // each so the (ntw-1)-tile halo of a segment stays a small share.
+        const long tiles_ub = ((long)a.total + (long)(kTile - 1) * a.B) / kTile;
+        long per = (tiles_ub * a.Hkv + 255) / 256;
+        per = per < 4 ? 4 : per;
+        per = per > cap_tiles ? cap_tiles : per;
+        const long nchunks = (tiles_ub + per - 1) / per;
+        dim3 grid((unsigned)nchunks, a.Hkv, 1);
+        hipLaunchKernelGGL((swa_prefill_ring_kernel<D, NW, true>), grid, dim3(NW * 64), 0, stream,
+                           (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
+                           (bf16 *)a.out, a.lse, a.S, a.Hq, a.Hkv, a.window, ntw,
+                           (int)per * kTile, a.cu_seqlens, a.B, a.total);
+        return hipGetLastError();
+    }
     const int tiles = (a.S + kTile - 1) / kTile;
     const int groups = a.B * a.Hkv;
     const int target = 256;                                   // one resident work-group per CU
@@ -378,13 +458,13 @@ hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
     per_group = max(1, min(per_group, tiles));
     int steps = (tiles + per_group - 1) / per_group;
     steps = max(steps, min(4, tiles));
-    const int ntw = (a.window - 1 + kTile - 1) / kTile + 1;
-    const int chunk = min(steps * kTile, prefill_chunk_cap(a.Hq, a.Hkv, a.D, ntw));
+    const int chunk = min(steps * kTile, cap_tiles * kTile);
     const int nchunks = (a.S + chunk - 1) / chunk;
     dim3 grid(nchunks, a.Hkv, a.B);
-    hipLaunchKernelGGL((swa_prefill_ring_kernel<D, NW>), grid, dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((swa_prefill_ring_kernel<D, NW, false>), grid, dim3(NW * 64), 0, stream,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
-                       (bf16 *)a.out, a.lse, a.S, a.Hq, a.Hkv, a.window, ntw, chunk);
+                       (bf16 *)a.out, a.lse, a.S, a.Hq, a.Hkv, a.window, ntw, chunk,
+                       (const int32_t *)nullptr, a.B, 0);
     return hipGetLastError();
 }
 

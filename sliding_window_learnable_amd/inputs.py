@@ -62,3 +62,19 @@ def cache_lengths(B: int, low: int, high: int, seed: int) -> torch.Tensor:
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
     return torch.randint(int(low), int(high) + 1, (B,), generator=gen, dtype=torch.int32)
+
+
+def packed_inputs(config: int, layer: int, lengths, Hq: int, Hkv: int, D: int,
+                  dtype=torch.bfloat16, device="cpu"):
+    """A packed batch of sequences of the given lengths: q [total, Hq, D],
+    k and v [total, Hkv, D] in ``dtype``, sink [Hq] float32 and cu_seqlens
+    int32 [B + 1] (row offsets of the sequences)."""
+    lengths = [int(n) for n in lengths]
+    total = sum(lengths)
+    q = randn((total, Hq, D), seed_for(config, layer, "q"), dtype, device)
+    k = randn((total, Hkv, D), seed_for(config, layer, "k"), dtype, device)
+    v = randn((total, Hkv, D), seed_for(config, layer, "v"), dtype, device)
+    sink = randn((Hq,), seed_for(config, layer, "sink"), torch.float32, device)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return q, k, v, sink, cu.to(device)

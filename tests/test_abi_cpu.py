@@ -248,3 +248,29 @@ def test_rope_append_rejects(lib, kw, code):
 def test_ring_calls_empty_are_noops(lib):
     assert dring(lib, B=0) == _lib.SWA_OK and dring(lib, T=0) == _lib.SWA_OK
     assert rapp(lib, B=0) == _lib.SWA_OK and rapp(lib, T=0) == _lib.SWA_OK
+
+
+def pvar(lib, q=P, k=P, v=P, sink=P, out=P, lse=None, cu=P, B=3, S=40, total=70, Hq=8, Hkv=1,
+         D=128, window=128, dtype=1):
+    return lib.swa_sink_prefill_varlen(q, k, v, sink, out, lse, cu, B, S, total, Hq, Hkv, D,
+                                       window, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.SWA_ERR_NULL), (dict(cu=None), _lib.SWA_ERR_NULL),
+    (dict(out=None), _lib.SWA_ERR_NULL),
+    (dict(B=-1), _lib.SWA_ERR_SHAPE), (dict(S=-1), _lib.SWA_ERR_SHAPE),
+    (dict(total=-5), _lib.SWA_ERR_SHAPE), (dict(window=0), _lib.SWA_ERR_SHAPE),
+    (dict(Hq=8, Hkv=3), _lib.SWA_ERR_SHAPE), (dict(B=70000), _lib.SWA_ERR_SHAPE),
+    (dict(B=60000, Hq=64, Hkv=8, S=1 << 30), _lib.SWA_ERR_SHAPE),
+    (dict(D=96), _lib.SWA_ERR_UNSUPPORTED), (dict(dtype=3), _lib.SWA_ERR_UNSUPPORTED),
+    (dict(cu=P + 2), _lib.SWA_ERR_UNSUPPORTED), (dict(k=P + 8), _lib.SWA_ERR_UNSUPPORTED),
+])
+def test_prefill_varlen_rejects(lib, kw, code):
+    assert pvar(lib, **kw) == code
+
+
+def test_prefill_varlen_empty_is_noop(lib):
+    assert pvar(lib, B=0) == _lib.SWA_OK
+    assert pvar(lib, S=0) == _lib.SWA_OK
+    assert pvar(lib, total=0) == _lib.SWA_OK
