@@ -78,6 +78,27 @@ def timed(fn, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def per_call(fn, batches, size):
+    """Median, p10 and p90 of the per-call time (us) over `batches` batches of
+    `size` back-to-back calls, each batch bracketed by HIP events on the
+    launch stream (an event between every call would add a gap per call and
+    change what is measured).  Run right after `timed`, with the clock warm."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for j in range(batches):
+        for i in range(size):
+            fn(j * size + i)
+        ev[j + 1].record(stream)
+    ev[batches].synchronize()
+    us = sorted(ev[j].elapsed_time(ev[j + 1]) * 1e3 / size for j in range(batches))
+    pick = lambda f: us[min(batches - 1, int(round(f * (batches - 1))))]
+    return {"median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9),
+            "batches": batches, "calls_per_batch": size}
+
+
 def sha256(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -111,7 +132,8 @@ def bench_prefill(args, swa, acc, torch):
     nbytes = acc.prefill_bytes(B, S, Hq, Hkv, D)
     tflops = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
-    res = dict(ms=ms, tflops=tflops, gbs=gbs, flops=flops, bytes=nbytes,
+    dist = per_call(lambda i: swa.swa_sink_prefill(q, k, v, sink, W, out=out, lse=lse), 20, 10)
+    res = dict(ms=ms, per_call=dist, tflops=tflops, gbs=gbs, flops=flops, bytes=nbytes,
                tokens_per_s=B * S / (ms * 1e-3),
                frac_mfma_peak=tflops / acc.PEAK_BF16_TFLOPS,
                frac_hbm_peak=gbs / acc.PEAK_HBM_GBS)
@@ -169,10 +191,11 @@ def bench_decode(args, swa, acc, torch):
         steps = max(200, 10 * args.steps)
         log("decode T_q=%d: %d calls" % (T, steps))
         ms = timed(call, steps, 200)
+        dist = per_call(call, 20, 50)
         nbytes = acc.decode_bytes(B, T, Hq, Hkv, W, D)
         flops = acc.decode_flops(B, T, Hq, D, W)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        res["T_q=%d" % T] = dict(us_per_call=ms * 1e3, hbm_gbs=gbs,
+        res["T_q=%d" % T] = dict(us_per_call=ms * 1e3, per_call=dist, hbm_gbs=gbs,
                                  frac_hbm_peak=gbs / acc.PEAK_HBM_GBS,
                                  tflops=flops / (ms * 1e-3) / 1e12,
                                  tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes)
