@@ -2,6 +2,7 @@
 fp64 oracle's packed prefill, on ragged length mixes."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
@@ -89,3 +90,30 @@ def test_rows_outside_sequences_untouched(gpu):
     torch.cuda.synchronize()
     assert torch.all(out[70:] == 7.0) and torch.all(lse[:, 70:] == 7.0)
     assert torch.all(out[:70] != 7.0)
+
+
+@pytest.mark.parametrize("global_layer", [False, True])
+def test_bucket_full_size_sampled_rows(gpu, global_layer):
+    """The benchmarked bucket (16 sequences, lengths uniform in [512, 8192],
+    Hq=64, Hkv=8, D=128), as bench.py launches it: every sequence's first two
+    and last two rows and six seeded random rows, all heads, against the
+    oracle over that sequence's own keys."""
+    Hq, Hkv, D = 64, 8, 128
+    lengths = [int(n) for n in inputs.cache_lengths(16, 512, 8192, seed=6000)]
+    S_max = max(lengths)
+    W = S_max if global_layer else 128
+    q, k, v, sink, cu = inputs.packed_inputs(6, 0, lengths, Hq, Hkv, D, torch.bfloat16, gpu)
+    print("varlen bucket", "global" if global_layer else "window 128", flush=True)
+    out, lse = swa.swa_sink_prefill_varlen(q, k, v, sink, cu, S_max, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6001)
+    offs = np.concatenate([[0], np.cumsum(lengths)])
+    for b, n in enumerate(lengths):
+        s0 = int(offs[b])
+        pos = np.unique(np.concatenate([[0, 1, n - 2, n - 1], rng.integers(0, n, 6)]))
+        idx = torch.as_tensor(s0 + pos, device=gpu)
+        ref_out, ref_lse = oracle.swa_prefill_rows(
+            to64(q.index_select(0, idx)), np.zeros(len(pos)), pos, to64(k[s0:s0 + n][None]),
+            to64(v[s0:s0 + n][None]), to64(sink), W)
+        check_out(out.index_select(0, idx), ref_out, torch.bfloat16)
+        check_lse(lse.index_select(1, idx).T, ref_lse, torch.bfloat16)
