@@ -54,6 +54,19 @@ def _check_device(*tensors):
             raise ValueError("every tensor must be contiguous")
 
 
+def _expect(t, shape, dtype, name):
+    """A caller-provided buffer must have exactly the shape and dtype the call
+    writes: the kernels trust the sizes they are given."""
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError("%s must be %s %s, got %s %s"
+                         % (name, dtype, tuple(shape), t.dtype, tuple(t.shape)))
+
+
+def _float32_sink(sink):
+    if sink.dtype != torch.float32:
+        raise TypeError("sink must be float32")
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -83,6 +96,8 @@ def swa_sink_prefill(q, k, v, sink, window: int, out=None, lse=None, want_lse: b
                          % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(sink.shape)))
     if sink.dtype != torch.float32:
         raise TypeError("sink must be float32")
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, S), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -112,6 +127,8 @@ def swa_sink_prefill_varlen(q, k, v, sink, cu_seqlens, max_seqlen: int, window: 
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be int32 [B + 1]")
     B = cu_seqlens.numel() - 1
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (Hq, total), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -138,6 +155,9 @@ def swa_sink_decode(q, kcache, vcache, sink, cache_len=None, out=None, lse=None,
         raise ValueError("shape mismatch")
     if cache_len is not None and (cache_len.dtype != torch.int32 or cache_len.shape != (B,)):
         raise ValueError("cache_len must be int32 [B]")
+    _float32_sink(sink)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, T), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -163,6 +183,9 @@ def swa_sink_decode_ring(q, kcache, vcache, sink, window: int, cache_len=None, o
         raise ValueError("shape mismatch")
     if cache_len is not None and (cache_len.dtype != torch.int32 or cache_len.shape != (B,)):
         raise ValueError("cache_len must be int32 [B]")
+    _float32_sink(sink)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, T), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -189,6 +212,7 @@ def swa_sink_rope_append(q, k_new, v_new, kcache, vcache, cache_len_old=None, ro
     if cache_len_old is not None and (cache_len_old.dtype != torch.int32
                                       or cache_len_old.shape != (B,)):
         raise ValueError("cache_len_old must be int32 [B]")
+    _expect(q_rot, q.shape, q.dtype, "q_rot")
     if q_rot is None:
         q_rot = torch.empty_like(q)
     _check_device(q, k_new, v_new, kcache, vcache, q_rot, cache_len_old)
@@ -214,6 +238,9 @@ def global_sink_attn(q, k, v, sink, out=None, lse=None, workspace=None, want_lse
     Skv, Hkv = k.shape[1], k.shape[2]
     if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
         raise ValueError("shape mismatch")
+    _float32_sink(sink)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Sq), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -242,12 +269,17 @@ def global_sink_attn_block_max(q, k, v, sink, block_k=128, out=None, lse=None, b
     Skv, Hkv = k.shape[1], k.shape[2]
     if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
         raise ValueError("shape mismatch")
+    _float32_sink(sink)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Sq), torch.float32, "lse")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    nkb = -(-Skv // block_k) if block_k > 0 else 0
+    _expect(block_max, (B, Hq, -(-Sq // 32), nkb), torch.float32, "block_max")
     if block_max is None:
-        block_max = torch.empty((B, Hq, -(-Sq // 32), -(-Skv // block_k)), device=q.device,
+        block_max = torch.empty((B, Hq, -(-Sq // 32), nkb), device=q.device,
                                 dtype=torch.float32)
     _check_device(q, k, v, sink, out, lse, block_max)
     dt = _dtype_code(q, k, v, out)
@@ -275,6 +307,12 @@ def swa_sink_backward(q, k, v, sink, out, lse, dout, window, dq=None, dk=None, d
     if (k.shape != (B, S, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,)
             or out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, S)):
         raise ValueError("shape mismatch")
+    _float32_sink(sink)
+    _expect(lse, (B, Hq, S), torch.float32, "lse")
+    _expect(dq, q.shape, q.dtype, "dq")
+    _expect(dk, k.shape, k.dtype, "dk")
+    _expect(dv, v.shape, v.dtype, "dv")
+    _expect(dsink, (Hq,), torch.float32, "dsink")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

@@ -155,6 +155,43 @@ def test_binding_refuses_cpu_tensors():
         swa.swa_sink_prefill(q, k, k, torch.zeros(8), 128)
 
 
+def test_binding_checks_caller_buffers():
+    """Output buffers the caller passes must match the shapes the call writes
+    (checked before anything reaches the library, so CPU tensors suffice)."""
+    import torch
+    import sliding_window_learnable_amd as swa
+    bf = torch.bfloat16
+    q = torch.zeros(2, 40, 8, 128, dtype=bf)
+    k = torch.zeros(2, 40, 2, 128, dtype=bf)
+    sink = torch.zeros(8)
+    cases = [
+        lambda: swa.swa_sink_prefill(q, k, k, sink, 128, out=torch.zeros(2, 39, 8, 128, dtype=bf)),
+        lambda: swa.swa_sink_prefill(q, k, k, sink, 128, out=torch.zeros_like(q, dtype=torch.float32)),
+        lambda: swa.swa_sink_prefill(q, k, k, sink, 128, lse=torch.zeros(2, 40, 8)),
+        lambda: swa.global_sink_attn(q, k, k, sink, lse=torch.zeros(2, 8, 40, dtype=torch.float64)),
+        lambda: swa.global_sink_attn_block_max(q, k, k, sink, 128, block_max=torch.zeros(2, 8, 2, 2)),
+        lambda: swa.swa_sink_prefill_varlen(q[0], k[0], k[0], sink,
+                                            torch.tensor([0, 40], dtype=torch.int32), 40, 128,
+                                            lse=torch.zeros(40, 8)),
+        lambda: swa.swa_sink_decode(q[:, :2], k.permute(0, 2, 1, 3).contiguous(),
+                                    k.permute(0, 2, 1, 3).contiguous(), sink,
+                                    lse=torch.zeros(2, 8, 3)),
+        lambda: swa.swa_sink_rope_append(q[:, :2], k[:, :2], k[:, :2],
+                                         k.permute(0, 2, 1, 3).contiguous(),
+                                         k.permute(0, 2, 1, 3).contiguous(),
+                                         q_rot=torch.zeros(2, 2, 8, 64, dtype=bf)),
+        lambda: swa.swa_sink_backward(q, k, k, sink, q, torch.zeros(2, 8, 40), q, 128,
+                                      dk=torch.zeros(2, 40, 8, 128, dtype=bf)),
+        lambda: swa.swa_sink_backward(q, k, k, sink, q, torch.zeros(2, 8, 40), q, 128,
+                                      dsink=torch.zeros(8, dtype=torch.float64)),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError):
+            call()
+    with pytest.raises(TypeError):               # the sink is float32
+        swa.global_sink_attn(q, k, k, sink.double())
+
+
 def bwd(lib, q=P, k=P, v=P, sink=P, out=P, lse=P, dout=P, dq=P, dk=P, dv=P, dsink=P, B=1, Hq=8,
         Hkv=1, S=16, D=128, window=128, ws=P, wsb=1 << 20, dtype=1):
     return lib.swa_sink_backward(q, k, v, sink, out, lse, dout, dq, dk, dv, dsink, B, Hq, Hkv, S, D,
