@@ -15,6 +15,8 @@ same JSON object:
                 and on a 16K global layer, with the forward time beside it
   varlen        packed prefill of 16 sequences of mixed length (one context
                 bucket), window 128 and global, against the padded batch
+  oracle_by_config  the fp64 oracle beside the GPU on every configuration above
+                (full or stated samples): time, GFLOP/s, speed-up, max |error|
 Inputs are seeded synthetic Gaussian tensors resident in HBM before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTION]
@@ -55,6 +57,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--oracle-ga-stride", type=int, default=256,
+                    help="query-row stride of the oracle's sample of the 64K global layer")
     return ap.parse_args()
 
 
@@ -137,7 +141,7 @@ def bench_prefill(args, swa, acc, torch):
                tokens_per_s=B * S / (ms * 1e-3),
                frac_mfma_peak=tflops / acc.PEAK_BF16_TFLOPS,
                frac_hbm_peak=gbs / acc.PEAK_HBM_GBS)
-    res["tensors"] = (q, k, v, sink)
+    res["tensors"] = (q, k, v, sink, out)
     return res
 
 
@@ -147,7 +151,7 @@ def bench_cpu_baseline(args, acc, torch, tensors):
     --cpu-seconds of CPU time has been spent."""
     import numpy as np
     import oracle
-    q, k, v, sink = tensors
+    q, k, v, sink, gpu_out = tensors
     B, S, Hq, D = q.shape
     W = 128
     q64 = q.double().cpu().numpy()
@@ -155,8 +159,10 @@ def bench_cpu_baseline(args, acc, torch, tensors):
     v64 = v.double().cpu().numpy()
     s64 = sink.double().cpu().numpy()
     t = time.perf_counter()
-    oracle.swa_prefill(q64, k64, v64, s64, W)
+    ref, _ = oracle.swa_prefill(q64, k64, v64, s64, W)
     first = time.perf_counter() - t
+    err = float(np.abs(gpu_out.double().cpu().numpy() - ref).max())
+    del ref
     reps = int(max(1, min(20, round(args.cpu_seconds / max(first, 1e-6)))))
     log("cpu baseline: one pass %.2fs, %d passes" % (first, reps))
     t = time.perf_counter()
@@ -165,7 +171,7 @@ def bench_cpu_baseline(args, acc, torch, tensors):
     dt = time.perf_counter() - t
     flops = reps * acc.prefill_flops(B, S, Hq, D, W)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "max_abs_err_vs_gpu": err,
             "sample": "%d full pass(es) of the 32K prefill workload (all 32768 rows, 64 heads), "
                       "fp64, %.1f s total" % (reps, dt),
             "seconds": dt}
@@ -425,6 +431,133 @@ def bench_varlen(args, swa, acc, torch):
     return res
 
 
+def bench_oracle_configs(args, swa, acc, torch, result):
+    """The fp64 oracle beside the GPU on every benchmarked configuration: wall
+    time on the host cores, GFLOP/s, the GPU's speed-up (GPU times from the
+    sections above) and the largest |GPU - oracle| over the compared outputs.
+    Full runs where they take seconds; stated row or sequence samples,
+    extrapolated by flops, for the 64K layers, the 256K prefill and the 256K
+    global decode.  Config 1 is also timed on one thread."""
+    import numpy as np
+    import oracle
+    from sliding_window_learnable_amd import inputs
+    f64 = lambda t: t.double().cpu().numpy()
+    nthreads = oracle.threads()
+    res = {"threads": nthreads, "affinity_cores": len(os.sched_getaffinity(0)),
+           "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+    def entry(oracle_s, flops, flops_total, gpu_s, err, sample):
+        scale = flops_total / flops
+        e = {"oracle_s": oracle_s, "oracle_gflops": flops / oracle_s / 1e9, "sample": sample,
+             "max_abs_err_vs_gpu": err}
+        if scale != 1.0:
+            e["oracle_s_extrapolated"] = oracle_s * scale
+        if gpu_s is not None:
+            e["gpu_s"] = gpu_s
+            e["gpu_speedup"] = oracle_s * scale / gpu_s
+        return e
+
+    def clock(fn):
+        t = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t
+
+    # 1: tiny fp32 reference and its variants; all threads, then one thread
+    q, k, v, sink = inputs.attention_inputs(1, 0, 1, 512, 512, 1, 1, 64, torch.float32, "cuda")
+    for name, W, sk in (("1", 128, None), ("1_sink=-inf", 128, float("-inf")),
+                        ("1_window=512", 512, None)):
+        sk_t = sink if sk is None else torch.full_like(sink, sk)
+        out, _ = swa.swa_sink_prefill(q, k, v, sk_t, W)
+        gpu_ms = timed(lambda i: swa.swa_sink_prefill(q, k, v, sk_t, W), 20, 5)
+        args64 = (f64(q), f64(k), f64(v), f64(sk_t), W)
+        (ref, _), dt = clock(lambda: oracle.swa_prefill(*args64))
+        fl = acc.prefill_flops(1, 512, 1, 64, W)
+        res[name] = entry(dt, fl, fl, gpu_ms * 1e-3, float(np.abs(f64(out) - ref).max()), "full")
+        if name == "1":
+            oracle.set_threads(1)
+            _, dt1 = clock(lambda: oracle.swa_prefill(*args64))
+            oracle.set_threads(nthreads)
+            res[name]["oracle_s_one_thread"] = dt1
+    log("oracle beside config 1 done")
+
+    # 3a / 3b: ring decode, full batch of one input set
+    for T in (1, 4):
+        q, kc, vc, sink = inputs.ring_inputs(3, 0, 256, T, 64, 8, 128, 128, torch.bfloat16, "cuda")
+        out, _ = swa.swa_sink_decode(q, kc, vc, sink)
+        (ref, _), dt = clock(lambda: oracle.ring_decode(f64(q), f64(kc), f64(vc), f64(sink)))
+        fl = acc.decode_flops(256, T, 64, 128, 128)
+        gpu = result.get("decode", {}).get("T_q=%d" % T, {}).get("us_per_call")
+        res["3_T_q=%d" % T] = entry(dt, fl, fl, None if gpu is None else gpu * 1e-6,
+                                    float(np.abs(f64(out) - ref).max()), "full (B=256)")
+        del q, kc, vc, sink, out
+    log("oracle beside config 3 done")
+
+    # 4: the 64K global layer on every 64th query row, all heads; the SWA
+    # layer on 4096 evenly spaced rows
+    S, Hq, Hkv, D = 65536, 64, 8, 128
+    q, k, v, sink = inputs.attention_inputs(4, 5, 1, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out, _ = swa.global_sink_attn(q, k, v, sink)
+    stride = max(1, int(args.oracle_ga_stride))
+    rows = np.arange(0, S, stride)
+    idx = torch.as_tensor(rows, device=q.device)
+    k64, v64 = f64(k[0][None]), f64(v[0][None])
+    (ref, _), dt = clock(lambda: oracle.global_rows(f64(q[0].index_select(0, idx)),
+                                                    np.zeros(len(rows)), rows, k64, v64, f64(sink)))
+    fl = int(4 * D * Hq * (rows + 1).sum())
+    gpu = result.get("hybrid_5to1", {}).get("global_layer_ms")
+    res["4_global_layer"] = entry(dt, fl, acc.global_flops(1, S, S, Hq, D),
+                                  None if gpu is None else gpu * 1e-3,
+                                  float(np.abs(f64(out[0].index_select(0, idx)) - ref).max()),
+                                  "every %dth query row (%d rows), all 64 heads; extrapolated by "
+                                  "flops" % (stride, len(rows)))
+    del q, k, v, sink, out, k64, v64
+    q, k, v, sink = inputs.attention_inputs(4, 0, 1, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out, _ = swa.swa_sink_prefill(q, k, v, sink, 128)
+    rows = np.arange(0, S, S // 4096)
+    idx = torch.as_tensor(rows, device=q.device)
+    (ref, _), dt = clock(lambda: oracle.swa_prefill_rows(
+        f64(q[0].index_select(0, idx)), np.zeros(len(rows)), rows, f64(k), f64(v), f64(sink), 128))
+    fl = int(4 * D * Hq * np.minimum(rows + 1, 128).sum())
+    gpu = result.get("hybrid_5to1", {}).get("swa_layer_ms")
+    res["4_swa_layer"] = entry(dt, fl, acc.prefill_flops(1, S, Hq, D, 128),
+                               None if gpu is None else gpu * 1e-3,
+                               float(np.abs(f64(out[0].index_select(0, idx)) - ref).max()),
+                               "4096 evenly spaced query rows, all heads; extrapolated by flops")
+    del q, k, v, sink, out
+    log("oracle beside config 4 done")
+
+    # 5a: 256K SWA prefill, 4096 rows; 5b: 256K global decode, sequence 0 of 8
+    S = 262144
+    q, k, v, sink = inputs.attention_inputs(5, 0, 1, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out, _ = swa.swa_sink_prefill(q, k, v, sink, 128)
+    rows = np.arange(0, S, S // 4096)
+    idx = torch.as_tensor(rows, device=q.device)
+    (ref, _), dt = clock(lambda: oracle.swa_prefill_rows(
+        f64(q[0].index_select(0, idx)), np.zeros(len(rows)), rows, f64(k), f64(v), f64(sink), 128))
+    fl = int(4 * D * Hq * np.minimum(rows + 1, 128).sum())
+    gpu = result.get("long_context", {}).get("swa_prefill_262144", {}).get("ms")
+    res["5a_swa_prefill_262144"] = entry(dt, fl, acc.prefill_flops(1, S, Hq, D, 128),
+                                         None if gpu is None else gpu * 1e-3,
+                                         float(np.abs(f64(out[0].index_select(0, idx)) - ref).max()),
+                                         "4096 evenly spaced query rows, all heads; extrapolated by flops")
+    del q, k, v, sink, out
+    q, k, v, sink = inputs.attention_inputs(5, 1, 8, 1, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    out, _ = swa.global_sink_attn(q, k, v, sink)
+    k64, v64 = f64(k[0:1]), f64(v[0:1])
+    (ref, _), dt = clock(lambda: oracle.global_rows(f64(q[0]), np.zeros(1), np.array([S - 1]),
+                                                    k64, v64, f64(sink)))
+    fl = acc.global_flops(1, 1, S, Hq, D)
+    gpu = result.get("long_context", {}).get("global_decode_B8_262144", {}).get("ms")
+    res["5b_global_decode_262144"] = entry(dt, fl, acc.global_flops(8, 1, S, Hq, D),
+                                           None if gpu is None else gpu * 1e-3,
+                                           float(np.abs(f64(out[0]) - ref).max()),
+                                           "sequence 0 of 8, all heads; extrapolated by flops")
+    del q, k, v, sink, out, k64, v64
+    torch.cuda.empty_cache()
+    log("oracle beside config 5 done")
+    return res
+
+
 def bench_copy(args, torch):
     """Plain 1 GiB device copy: the reference kernel for scaling PMC byte counters."""
     n = 1 << 30
@@ -499,6 +632,8 @@ def main():
         result["backward"] = bench_backward(args, swa, acc, torch)
     if args.only in ("all", "varlen"):
         result["varlen"] = bench_varlen(args, swa, acc, torch)
+    if args.only == "all" and not args.no_cpu_baseline:
+        result["oracle_by_config"] = bench_oracle_configs(args, swa, acc, torch, result)
     print(json.dumps(result))
 
 

@@ -70,6 +70,8 @@ def bind(path: str):
     lib.oracle_count_window_pairs.restype = i64
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     return lib
 
 
@@ -296,3 +298,8 @@ def count_window_pairs(S: int, W: int) -> int:
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's later parallel loops (timing runs only)."""
+    _load().oracle_set_threads(int(n))

@@ -365,6 +365,16 @@ int64_t oracle_count_window_pairs(int64_t S, int64_t W)
     return total;
 }
 
+/* Sets the threads later parallel regions use (n >= 1); timing only. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads an OpenMP parallel region of the oracle uses. */
 int oracle_threads(void)
 {
