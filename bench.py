@@ -140,7 +140,8 @@ def bench_prefill(args, swa, acc, torch):
     res = dict(ms=ms, per_call=dist, tflops=tflops, gbs=gbs, flops=flops, bytes=nbytes,
                tokens_per_s=B * S / (ms * 1e-3),
                frac_mfma_peak=tflops / acc.PEAK_BF16_TFLOPS,
-               frac_hbm_peak=gbs / acc.PEAK_HBM_GBS)
+               frac_hbm_peak=gbs / acc.PEAK_HBM_GBS,
+               frac_roofline=acc.roofline_frac(flops, nbytes, ms * 1e-3))
     res["tensors"] = (q, k, v, sink, out)
     return res
 
@@ -203,6 +204,7 @@ def bench_decode(args, swa, acc, torch):
         gbs = nbytes / (ms * 1e-3) / 1e9
         res["T_q=%d" % T] = dict(us_per_call=ms * 1e3, per_call=dist, hbm_gbs=gbs,
                                  frac_hbm_peak=gbs / acc.PEAK_HBM_GBS,
+                                 frac_roofline=acc.roofline_frac(flops, nbytes, ms * 1e-3),
                                  tflops=flops / (ms * 1e-3) / 1e12,
                                  tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes)
         del sets, outs, lses
@@ -288,6 +290,10 @@ def bench_hybrid(args, swa, acc, torch):
         "swa_layer_tflops": f_swa / (ms_swa5 / 5 * 1e-3) / 1e12,
         "global_layer_tflops": f_ga / (ms_ga * 1e-3) / 1e12,
         "global_layer_frac_mfma_peak": f_ga / (ms_ga * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
+        "global_layer_frac_roofline": acc.roofline_frac(
+            f_ga, acc.global_bytes(B, S, S, Hq, Hkv, D), ms_ga * 1e-3),
+        "swa_layer_frac_roofline": acc.roofline_frac(
+            f_swa, acc.prefill_bytes(B, S, Hq, Hkv, D), ms_swa5 / 5 * 1e-3),
         "swa_layer_hbm_gbs": acc.prefill_bytes(B, S, Hq, Hkv, D) / (ms_swa5 / 5 * 1e-3) / 1e9,
         "flop_ratio_swa_over_global_per_layer": f_swa / f_ga,
         "flop_share_of_5_swa_layers": 5 * f_swa / (5 * f_swa + f_ga),
@@ -321,6 +327,7 @@ def bench_long(args, swa, acc, torch):
     res["swa_prefill_262144"] = dict(ms=ms, tflops=f / (ms * 1e-3) / 1e12,
                                      hbm_gbs=nb / (ms * 1e-3) / 1e9,
                                      frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+                                     frac_roofline=acc.roofline_frac(f, nb, ms * 1e-3),
                                      tokens_per_s=S / (ms * 1e-3))
     del q, k, v, out, lse
     torch.cuda.empty_cache()
@@ -336,6 +343,7 @@ def bench_long(args, swa, acc, torch):
     nb = acc.global_bytes(B, Sq, Skv, Hq, Hkv, D)
     res["global_decode_B8_262144"] = dict(
         ms=ms, hbm_gbs=nb / (ms * 1e-3) / 1e9, frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+        frac_roofline=acc.roofline_frac(acc.global_flops(B, Sq, Skv, Hq, D), nb, ms * 1e-3),
         tokens_per_s=B / (ms * 1e-3),
         kv_bytes_per_sequence_vs_swa_ring=Skv / 128)
     return res
@@ -372,6 +380,7 @@ def bench_backward(args, swa, acc, torch):
         nb = acc.backward_bytes(B, S, Hq, Hkv, D)
         res[name] = dict(ms=ms_b, tflops=fl / (ms_b * 1e-3) / 1e12,
                          frac_mfma_peak=fl / (ms_b * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
+                         frac_roofline=acc.roofline_frac(fl, nb, ms_b * 1e-3),
                          hbm_gbs=nb / (ms_b * 1e-3) / 1e9, forward_ms=ms_f,
                          backward_over_forward=ms_b / ms_f, tokens_per_s=B * S / (ms_b * 1e-3))
         del q, k, v, sink, g, out, lse, dq, dk, dv, dsink, ws
@@ -406,7 +415,8 @@ def bench_varlen(args, swa, acc, torch):
                          tflops=fl / (ms * 1e-3) / 1e12,
                          frac_mfma_peak=fl / (ms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
                          hbm_gbs=nb / (ms * 1e-3) / 1e9,
-                         frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS)
+                         frac_hbm_peak=nb / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBS,
+                         frac_roofline=acc.roofline_frac(fl, nb, ms * 1e-3))
     del out, lse
     # the same sequences padded on the right to S_max, as a [B, S_max] batch
     qp = torch.zeros((B, S_max, Hq, D), device="cuda", dtype=torch.bfloat16)

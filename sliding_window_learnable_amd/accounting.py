@@ -23,6 +23,13 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_F32_MFMA_TFLOPS = 157.3
 
 
+def roofline_frac(flops: float, nbytes: float, seconds: float) -> float:
+    """Achieved flops over the roofline min(bf16 MFMA peak, AI * HBM peak),
+    AI = flops / bytes (algorithmic)."""
+    roof = min(PEAK_BF16_TFLOPS * 1e12, flops / nbytes * PEAK_HBM_GBS * 1e9)
+    return flops / seconds / roof
+
+
 def window_pairs(S: int, W: int) -> int:
     """(row, key) pairs of a causal window-W layer over S tokens."""
     m = min(S, W)

@@ -46,3 +46,16 @@ def test_hybrid_reductions_near_pages_six_fold():
     # the plain formula gives 8x for a 7:1 schedule (the talk quotes 7x)
     compute7, _ = acc.hybrid_ratios(262144, 128, 7)
     assert 7.9 < compute7 < 8.0
+
+
+def test_roofline_fraction_is_one_at_the_bound():
+    """At the ideal time of the binding resource the fraction is exactly 1:
+    HBM for the 32K window-128 prefill (AI ~ 113 flop/B), MFMA for the 64K
+    global layer."""
+    f = acc.prefill_flops(1, 32768, 64, 128, 128)
+    b = acc.prefill_bytes(1, 32768, 64, 8, 128)
+    assert abs(acc.roofline_frac(f, b, b / (acc.PEAK_HBM_GBS * 1e9)) - 1.0) < 1e-12
+    assert abs(acc.roofline_frac(f, b, 2 * b / (acc.PEAK_HBM_GBS * 1e9)) - 0.5) < 1e-12
+    f = acc.global_flops(1, 65536, 65536, 64, 128)
+    b = acc.global_bytes(1, 65536, 65536, 64, 8, 128)
+    assert abs(acc.roofline_frac(f, b, f / (acc.PEAK_BF16_TFLOPS * 1e12)) - 1.0) < 1e-12
