@@ -138,6 +138,8 @@ def bench_prefill(args, swa, acc, torch):
     gbs = nbytes / (ms * 1e-3) / 1e9
     dist = per_call(lambda i: swa.swa_sink_prefill(q, k, v, sink, W, out=out, lse=lse), 20, 10)
     res = dict(ms=ms, per_call=dist, tflops=tflops, gbs=gbs, flops=flops, bytes=nbytes,
+               cache="one input set: its 1.2 GB of inputs and outputs exceed the 256 MB "
+                     "Infinity Cache",
                tokens_per_s=B * S / (ms * 1e-3),
                frac_mfma_peak=tflops / acc.PEAK_BF16_TFLOPS,
                frac_hbm_peak=gbs / acc.PEAK_HBM_GBS,
