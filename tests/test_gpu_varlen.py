@@ -37,6 +37,9 @@ CASES = [
     ([0, 0, 45], 4, 4, 128, 1),
     ([150, 90, 211], 8, 1, 128, 100000),      # window past every length: causal per sequence
     ([64, 64, 64, 64], 6, 2, 64, 64),
+    ([77, 300, 1], 4, 2, 128, 128),            # packed ring kernel, GQA group 2
+    ([65, 129, 0, 250], 8, 2, 64, 100),        # packed ring kernel, group 4, D=64, window 100
+    ([40, 700], 4, 4, 128, 98),                # packed ring kernel, group 1, shortest ring window
 ]
 
 
