@@ -24,6 +24,9 @@
 // tile t-1 freed.  One barrier per tile.  Work-groups are issued longest-first
 // (the last query blocks have the most keys) with the (batch, KV head)
 // index fastest, so the blocks of one KV head share an XCD and its L2.
+// Packed batches of sequences of different lengths give each work-group its
+// sequence's first row and length from the row-offset table; blocks past a
+// sequence's end return before touching memory or a barrier.
 #include "attn_device.h"
 #include "launch.h"
 

@@ -19,6 +19,12 @@
 //    band mask, one softmax pass seeded with the sink (running max starts at
 //    s_h, denominator at exp(s_h - max)), O^T = V^T P^T on MFMA, then
 //    out = O / l (bf16, RNE) and lse = max + ln l.
+//  * packed batches of sequences of different lengths (serving mixed
+//    context lengths together: "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？|
+//    ICML 2026", §06 Q&A) use the same step code: the concatenation of every
+//    sequence's 32-row tiles is split evenly over the work-groups, and a
+//    work-group runs one segment per sequence its share meets, each segment
+//    starting with its own (window-1)-key halo.
 #include "attn_device.h"
 #include "launch.h"
 
