@@ -214,17 +214,33 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
             lds_barrier();                                 // tile t's slot released
         }
 
-        if (row_ok) {
-            bf16 *orow = dq + (((size_t)b * S + i) * Hq + h) * D;
+        // dq rows through this wave's 32 x D area of the (now idle) K/V
+        // slots, stored as whole rows: 16 bytes per lane, CPR lanes a row.
+        {
+            static_assert(sizeof(sm.k) + sizeof(sm.v) >= (size_t)NW * kTile * D * 2, "staging");
+            bf16 (*stg)[D] = reinterpret_cast<bf16 (*)[D]>(reinterpret_cast<char *>(&sm)) +
+                             wave * kTile;            // K then V slots, from the start of sm
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt) {
+                u32x2 w[4];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     bf16x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[dt][4 * jj + e] * scale);
-                    *(bf16x4 *)(orow + 32 * dt + 8 * jj + 4 * hl) = x;
+                    w[jj] = __builtin_bit_cast(u32x2, x);
+                    const int cidx = 4 * dt + jj;                 // 16-byte chunk of dims 8*cidx..
+                    *(u32x2 *)&stg[lq][8 * (cidx ^ swz<D>(lq)) + 4 * hl] = w[jj];
                 }
+                lds_settle(w);
+            }
+#pragma unroll
+            for (int u = 0; u < kTile / RPI; ++u) {
+                const int r = RPI * u + lane / CPR, cidx = lane % CPR;
+                const bf16x8 y = *(const bf16x8 *)&stg[r][8 * (cidx ^ swz<D>(r))];
+                if (i0 + r < S)
+                    *(bf16x8 *)(dq + (((size_t)b * S + i0 + r) * Hq + h) * D + 8 * cidx) = y;
+            }
         }
     }
 }
@@ -468,19 +484,36 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
         }
     }
 
-    if (wave_ok && j0 + lq < S) {
-        const size_t off = (((size_t)b * S + j0 + lq) * Hkv + g) * D;
+    // dk / dv rows through this wave's 32 x D area of the (now idle) Q/dO
+    // slots, stored as whole rows: 16 bytes per lane, CPR lanes a row.
+    if (wave_ok) {
         bf16 *dst = role_s ? dv : dk;
         const float f = role_s ? 1.0f : scale;
+        static_assert(sizeof(sm.q) + sizeof(sm.g) >= (size_t)2 * NW * kTile * D * 2, "staging");
+        bf16 (*stg)[D] = reinterpret_cast<bf16 (*)[D]>(reinterpret_cast<char *>(&sm)) +
+                         wave * kTile;                // Q then dO slots, from the start of sm
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt) {
+            u32x2 w[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 bf16x4 xo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) xo[e] = (bf16)(acc[dt][4 * jj + e] * f);
-                *(bf16x4 *)(dst + off + 32 * dt + 8 * jj + 4 * hl) = xo;
+                w[jj] = __builtin_bit_cast(u32x2, xo);
+                const int cidx = 4 * dt + jj;
+                *(u32x2 *)&stg[lq][8 * (cidx ^ swz<D>(lq)) + 4 * hl] = w[jj];
             }
+            lds_settle(w);
+        }
+        constexpr int CPR2 = D / 8, RPI2 = 64 / CPR2;
+#pragma unroll
+        for (int u = 0; u < kTile / RPI2; ++u) {
+            const int r = RPI2 * u + lane / CPR2, cidx = lane % CPR2;
+            const bf16x8 y = *(const bf16x8 *)&stg[r][8 * (cidx ^ swz<D>(r))];
+            if (j0 + r < S)
+                *(bf16x8 *)(dst + (((size_t)b * S + j0 + r) * Hkv + g) * D + 8 * cidx) = y;
+        }
     }
 }
 
