@@ -124,6 +124,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
         const int h = g * G + hh;
         if (hh != wave) lds_barrier();                     // previous head's tiles released
 
+        // K/V tiles 0..2 start copying before the row loads, so the two
+        // latencies overlap.
+        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
         bf16x8 qf[D / 16], gf[D / 16];
         float dsum_part = 0.0f;
         {
@@ -162,7 +165,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
             retire(gf[ks]);
         }
 
-        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
         dma_wait(false);
         lds_barrier();
 
@@ -416,9 +418,9 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
         else if (slot == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW + 1) : "memory");
         else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
     };
+    for (int n = 0; n < 3 && n < N; ++n) stage(n);       // overlaps the K/V row loads
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) retire(kvf[ks]);
-    for (int n = 0; n < 3 && n < N; ++n) stage(n);
     dma_wait(false);
     lds_barrier();
 
