@@ -139,6 +139,9 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     for (int hh = wave; hh < G; hh += NW) {
         const int h = g * G + hh;
         if (hh != wave) lds_barrier();                 // previous head's reads are done
+        // Tiles 0, 1 (and 2, left in flight) start copying into slots 0, 1, 2
+        // before the Q loads, so the two latencies overlap.
+        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
         bf16x8 qf[D / 16];
         {
             const bf16 *qrow = q + ((q_row0 + min(i, S_q - 1)) * Hq + h) * D + 8 * hl;
@@ -147,8 +150,6 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) retire(qf[ks]);
         }
-        // Prologue: tiles 0, 1 (and 2, left in flight) into slots 0, 1, 2.
-        for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
         if (n_tiles > 2) dma_wait(true);
         else dma_wait(false);
         const float s2 = sink[h] * kLog2e;
