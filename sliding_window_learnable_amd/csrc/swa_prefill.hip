@@ -407,13 +407,26 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         vr = make_rsrc(v + ((row0 + r0) * Hkv + g) * D, (c1 - r0) * rs);
         lr = make_rsrc(lrow != nullptr ? lrow + c0 : nullptr,
                        lrow != nullptr ? (uint32_t)(c1 - c0) * 4 : 0u);
-        for (int T = T_first; T <= c0 / kTile; ++T) {
-            st.load(kr, vr, rs, kTile * T - r0, tid);
-            st.store(sm, T % R, tid);
-        }
-
         bf16x8 qa[D / 16], qb[D / 16];
-        load_q(qa, c0);
+        if constexpr (!PACKED) {
+            // The first step's Q and every window tile up to the step's own
+            // are all requested before any is waited for.
+            load_q(qa, c0);
+            Stager<D, NT> pro[kMaxTiles];
+            const int n_pro = c0 / kTile - T_first + 1;   // <= ntw <= kMaxTiles
+#pragma unroll
+            for (int u = 0; u < kMaxTiles; ++u)
+                if (u < n_pro) pro[u].load(kr, vr, rs, kTile * (T_first + u) - r0, tid);
+#pragma unroll
+            for (int u = 0; u < kMaxTiles; ++u)
+                if (u < n_pro) pro[u].store(sm, (T_first + u) % R, tid);
+        } else {
+            for (int T = T_first; T <= c0 / kTile; ++T) {
+                st.load(kr, vr, rs, kTile * T - r0, tid);
+                st.store(sm, T % R, tid);
+            }
+            load_q(qa, c0);
+        }
         for (int p0 = c0; p0 < c1; p0 += 2 * kTile) {
             step(qa, qb, p0);
             if (p0 + kTile >= c1) break;
