@@ -45,6 +45,8 @@ CASES = [
     (1, 1000, 64, 8, 128, 128),
     (3, 77, 4, 2, 64, 1),          # every row sees only itself
     (1, 333, 16, 2, 128, 100),
+    (1, 200, 16, 1, 128, 128),     # two query heads per wave (G = 16)
+    (2, 130, 32, 2, 64, 64),       # G = 16 at D = 64
 ]
 
 
