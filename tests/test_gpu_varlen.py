@@ -120,3 +120,18 @@ def test_bucket_full_size_sampled_rows(gpu, global_layer):
             to64(v[s0:s0 + n][None]), to64(sink), W)
         check_out(out.index_select(0, idx), ref_out, torch.bfloat16)
         check_lse(lse.index_select(1, idx).T, ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("W", [128, 33])
+def test_table_entries_are_clamped(gpu, W):
+    """Offsets below 0 or past `total` are clamped by the kernels (no access
+    leaves the tensors): [-5, 30, 500] over 100 rows runs as [0, 30, 100]."""
+    lengths = [30, 70]
+    q, k, v, sink, cu = inputs.packed_inputs(93, 0, lengths, 8, 2, 128, torch.bfloat16)
+    ref_out, ref_lse = oracle.prefill_varlen(to64(q), to64(k), to64(v), to64(sink), cu.numpy(), W)
+    bad = torch.tensor([-5, 30, 500], dtype=torch.int32)
+    out, lse = swa.swa_sink_prefill_varlen(q.to(gpu), k.to(gpu), v.to(gpu), sink.to(gpu),
+                                           bad.to(gpu), 70, W)
+    torch.cuda.synchronize()
+    check_out(out, ref_out, torch.bfloat16)
+    check_lse(lse, ref_lse, torch.bfloat16)
