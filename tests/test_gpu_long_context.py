@@ -1,0 +1,51 @@
+"""GPU parity at the long-context sizes: the 262144-token window-128 prefill
+(its chunk buffer windows near the 31-bit range limit) on sampled rows, and
+the global decode of 8 sequences over 262144 keys (split-KV partials plus
+combine) on one full sequence, against the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_learnable_amd as swa
+from sliding_window_learnable_amd import inputs
+from tests.parity import check_lse, check_out, to64
+
+pytestmark = pytest.mark.gpu
+
+S_LONG = 262144
+
+
+def test_swa_prefill_262144_sampled_rows(gpu):
+    """First and last 256 rows, 2048 seeded random rows, all 64 heads."""
+    B, Hq, Hkv, D, W = 1, 64, 8, 128, 128
+    print("prefill 262144", flush=True)
+    q, k, v, sink = inputs.attention_inputs(5, 0, B, S_LONG, S_LONG, Hq, Hkv, D, torch.bfloat16,
+                                            gpu)
+    out, lse = swa.swa_sink_prefill(q, k, v, sink, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5001)
+    rows = np.array(sorted(set(range(256)) | set(range(S_LONG - 256, S_LONG))
+                           | set(rng.integers(0, S_LONG, 2048).tolist())))
+    idx = torch.as_tensor(rows, device=gpu)
+    ref_out, ref_lse = oracle.swa_prefill_rows(to64(q[0].index_select(0, idx)),
+                                               np.zeros(len(rows)), rows, to64(k), to64(v),
+                                               to64(sink), W)
+    check_out(out[0].index_select(0, idx), ref_out, torch.bfloat16)
+    check_lse(lse[0].index_select(1, idx).T, ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("seq", [0, 7])
+def test_global_decode_262144_one_sequence(gpu, seq):
+    """One of the 8 sequences in full (all 64 heads), as the bench launches it."""
+    B, Hq, Hkv, D = 8, 64, 8, 128
+    print("global decode 262144, sequence", seq, flush=True)
+    q, k, v, sink = inputs.attention_inputs(5, 1, B, 1, S_LONG, Hq, Hkv, D, torch.bfloat16, gpu)
+    out, lse = swa.global_sink_attn(q, k, v, sink)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.global_rows(to64(q[seq]), np.zeros(1), np.array([S_LONG - 1]),
+                                          to64(k[seq:seq + 1]), to64(v[seq:seq + 1]), to64(sink))
+    check_out(out[seq], ref_out, torch.bfloat16)
+    check_lse(lse[seq].T, ref_lse, torch.bfloat16)
