@@ -116,17 +116,30 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
         dma_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
     }
+    // When the whole key range of the sequence fits one descriptor's 32-bit
+    // range, the descriptors are built once and a tile's offset rides in the
+    // per-lane offset (range-checked, so rows past the end still land as
+    // zero); otherwise each tile gets descriptors of its own.
+    const bool one_rsrc = (unsigned long long)(S_kv + kTile) * rs <= (1ull << 32);   // no offset wraps
+    const uint32_t seq_bytes = one_rsrc && S_kv > 0 ? (uint32_t)(S_kv - 1) * rs + D * 2 : 0u;
+    const u32x4 k_all = sgpr_rsrc(kb, seq_bytes), v_all = sgpr_rsrc(vb, seq_bytes);
     auto stage = [&](int T, int slot) {
-        const int rows = min(kTile, S_kv - kTile * T);
-        const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * rs + D * 2 : 0u;
-        const size_t to = (size_t)kTile * T * row_elems;
-        const u32x4 kr = sgpr_rsrc(kb + to, bytes), vr = sgpr_rsrc(vb + to, bytes);
+        u32x4 kr = k_all, vr = v_all;
+        uint32_t to_b = (uint32_t)(kTile * T) * rs;
+        if (!one_rsrc) {
+            const int rows = min(kTile, S_kv - kTile * T);
+            const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * rs + D * 2 : 0u;
+            const size_t to = (size_t)kTile * T * row_elems;
+            kr = sgpr_rsrc(kb + to, bytes);
+            vr = sgpr_rsrc(vb + to, bytes);
+            to_b = 0;
+        }
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
             const int ii = wave * IPW + u;             // uniform
             const bool is_k = ii < NI / 2;
             bf16(*tile)[D] = is_k ? sm.k[slot] : sm.v[slot];
-            dma16(is_k ? kr : vr, tile[(ii % (NI / 2)) * RPI], dma_off[u]);
+            dma16(is_k ? kr : vr, tile[(ii % (NI / 2)) * RPI], dma_off[u] + to_b);
         }
     };
     auto dma_wait = [&](bool newer) {
