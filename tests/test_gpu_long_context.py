@@ -1,7 +1,8 @@
 """GPU parity at the long-context sizes: the 262144-token window-128 prefill
 (its chunk buffer windows near the 31-bit range limit) on sampled rows, and
 the global decode of 8 sequences over 262144 keys (split-KV partials plus
-combine) on one full sequence, against the fp64 oracle."""
+combine) on one full sequence, and the streaming kernel past 32-bit key
+offsets, against the fp64 oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -12,6 +13,7 @@ import oracle
 import sliding_window_learnable_amd as swa
 from sliding_window_learnable_amd import inputs
 from tests.parity import check_lse, check_out, to64
+from tests.test_gpu_block_max import check_bmax
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +51,25 @@ def test_global_decode_262144_one_sequence(gpu, seq):
                                           to64(k[seq:seq + 1]), to64(v[seq:seq + 1]), to64(sink))
     check_out(out[seq], ref_out, torch.bfloat16)
     check_lse(lse[seq].T, ref_lse, torch.bfloat16)
+
+
+def test_stream_kernel_keys_past_32bit_offsets(gpu):
+    """Keys whose byte offsets within one KV head's column pass 2^32 (2^21 + 37
+    positions of 8 KV heads x 128 dims): the streaming kernel then builds its
+    copy descriptors per tile.  All 69 query rows (3 blocks, ragged) of the
+    two query heads of KV head 0, with their block maxima."""
+    B, Hq, Hkv, D, S_q, bk = 1, 16, 8, 128, 69, 128
+    S_kv = (1 << 21) + 37
+    assert (S_kv + 32) * Hkv * D * 2 > (1 << 32)
+    print("block-max global over", S_kv, "keys", flush=True)
+    q, k, v, sink = inputs.attention_inputs(5, 2, B, S_q, S_kv, Hq, Hkv, D, torch.bfloat16, gpu)
+    out, lse, bm = swa.global_sink_attn_block_max(q, k, v, sink, block_k=bk)
+    torch.cuda.synchronize()
+    k0, v0 = to64(k[:, :, 0:1]), to64(v[:, :, 0:1])
+    del k, v
+    rows = np.arange(S_kv - S_q, S_kv)
+    ref_out, ref_lse = oracle.global_rows(to64(q[0, :, 0:2]), np.zeros(S_q), rows, k0, v0,
+                                          to64(sink[0:2]))
+    check_out(out[0, :, 0:2], ref_out, torch.bfloat16)
+    check_lse(lse[0, 0:2].T, ref_lse, torch.bfloat16)
+    check_bmax(bm[:, 0:2], oracle.block_max(to64(q[:, :, 0:2]), k0, bk))
