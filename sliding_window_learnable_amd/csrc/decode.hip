@@ -145,11 +145,19 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     // The refill is unconditional: past the item's keys the loads are out
     // of the descriptor's range and return zeros without touching memory.
     // K before V everywhere, so that the S^T products wait only for K.
-    load_k(0);
+    // Neighbouring waves start at different chunks of their keys (the order
+    // of the chunks does not matter to the online softmax), so that the
+    // requests in flight at any moment spread over more address offsets.
+    const int rot = n_chunks > 0 ? item % n_chunks : 0;
+    load_k(kChunk * rot);
     __builtin_amdgcn_sched_barrier(0);
-    load_v(0);
+    load_v(kChunk * rot);
     for (int ci = 0; ci < n_chunks; ++ci) {
-        const int k0 = kChunk * ci;
+        const int cc = ci + rot < n_chunks ? ci + rot : ci + rot - n_chunks;
+        const int k0 = kChunk * cc;
+        // The next chunk; after the last, an offset past the item's keys
+        // (the loads then return zeros without touching memory).
+        const int cn = ci + 1 == n_chunks ? n_chunks : (cc + 1 < n_chunks ? cc + 1 : 0);
 
         // Stage this chunk: K rows as they are, V transposed.  The previous
         // chunk's PV products may still be running, so lds_settle holds the
@@ -178,8 +186,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
             }
             lds_settle(w);
         }
-        load_k(k0 + kChunk);
-        load_v(k0 + kChunk);
+        load_k(kChunk * cn);
+        load_v(kChunk * cn);
 
         // S^T = K Q^T: A row lq is key score_row_key(lq), lane half hl
         // feeds dims [D/2*hl, D/2*hl + D/2) like the Q fragments.
