@@ -40,7 +40,14 @@
  *    aligned; sink, lse and cache_len 4-byte aligned (SWA_ERR_UNSUPPORTED).
  *  - GQA: Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv).
  *  - Softmax scale is fixed at 1/sqrt(D).
- *  - Sink values must be finite or -inf (NaN propagates; +inf is undefined).
+ *  - Sink values must be finite or -inf (+inf is undefined).
+ *  - Non-finite inputs are not clamped: a NaN sink makes every output of its
+ *    head NaN (lse too; a row with no visible key keeps out = 0), a NaN in
+ *    a query row makes that row's out and lse NaN, a NaN in a key row makes
+ *    out and lse NaN for exactly the rows that see that key.  A non-finite
+ *    value row makes out NaN for the rows that see it and may also reach
+ *    rows of the same 32-key tile that do not (their weight for it is 0,
+ *    and 0 * NaN = NaN in the matrix products); lse is unaffected.
  *  - Supported head dims: D in {64, 128}.
  *  - bfloat16 results are rounded to nearest-even from float32 accumulators.
  */
@@ -133,7 +140,9 @@ SWA_API int swa_sink_prefill_varlen(const void *q, const void *k, const void *v,
  * Query t is at position p = L - T_q + t and sees positions max(0, L-window)
  * .. p (older positions were overwritten).  With a full ring, draft t sees
  * window - (T_q - 1 - t) keys.  Rows with p < 0 see no key (out = 0).
- * Requires T_q <= window.  The kernel never reads a slot outside the ring.
+ * Requires T_q <= window.  The kernel never reads a slot outside the ring,
+ * and while the ring is not yet full (L < window) it never reads the slots
+ * L .. window-1 that no token has reached, whatever they hold.
  */
 SWA_API int swa_sink_decode(const void *q, const void *kcache, const void *vcache,
                     const float *sink, void *out, float *lse, int B, int Hq, int Hkv,
@@ -155,6 +164,7 @@ SWA_API int swa_sink_decode(const void *q, const void *kcache, const void *vcach
  * rejected (the caller rolls back by lowering its token count; the rejected
  * slots are rewritten by the next append).  ring == window is exactly
  * swa_sink_decode.  Requires window >= 1, ring >= window, T_q <= ring.
+ * Before the ring fills (L < ring) the slots L .. ring-1 are never read.
  * Other arguments and results as for swa_sink_decode.
  */
 SWA_API int swa_sink_decode_ring(const void *q, const void *kcache, const void *vcache,
@@ -173,6 +183,9 @@ SWA_API int swa_sink_decode_ring(const void *q, const void *kcache, const void *
  *   kcache, vcache [B, Hkv, ring, D]
  *   cache_len_old [B] (device, int32; NULL: 0): tokens in the cache before
  *                 this step; token t is at position P = cache_len_old + t
+ *                 (a negative entry is not an error the kernel can report:
+ *                 its slots are taken as P mod ring in [0, ring), so the
+ *                 writes stay inside that sequence's ring)
  * Rotation: dimension i (< D/2) pairs with i + D/2 at angle
  * P * rope_theta^(-2i/D):  y_i = x_i cos - x_{i+D/2} sin,
  * y_{i+D/2} = x_{i+D/2} cos + x_i sin (angles reduced in double precision,

@@ -238,8 +238,4 @@ hipError_t launch_backward_dsink(const BackwardArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_backward_bf16_rowwise(const BackwardArgs &a, hipStream_t stream) {
-    return launch_generic<bf16>(a, stream);
-}
-
 }  // namespace swa

@@ -86,7 +86,11 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
         rs = (uint32_t)D * 2;
         kbase = kc + ((size_t)b * Hkv + g) * (size_t)W * D;
         vbase = vc + ((size_t)b * Hkv + g) * (size_t)W * D;
-        kv_bytes = (uint32_t)W * rs;
+        // Until the ring has wrapped (L < W) only slots 0 .. L-1 have been
+        // written: the range stops there, so the unwritten slots read as
+        // zeros and whatever bits they hold never reach a product (a masked
+        // key's zero weight times a non-finite value would still be NaN).
+        kv_bytes = (uint32_t)min(max(L, 0), W) * rs;
     } else {
         const int k_begin = split * kps;
         n_keys = min(S_kv, k_begin + kps) - k_begin;
@@ -134,7 +138,10 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
 
     float m = -INFINITY;                              // running max (log2 units)
     const float s2 = sink[h] * kLog2e;
-    if (RING) m = s2;                                 // sink-seeded
+    // Sink-seeded; a NaN sink is left out of the max so that it reaches the
+    // results only through the denominator (as in the definition: a row
+    // with no visible key then keeps out = 0, and lse becomes NaN).
+    if (RING && !__builtin_isnan(s2)) m = s2;
     float l = 0.0f;                                   // this lane's share of the real-token sum
     f32x16 o[D / 32];
 #pragma unroll
@@ -237,8 +244,10 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     const float lsum = wave_xor32_sum(l);
     if (RING) {
         // The sink joins the denominator once: l = sum_j e^{x_j - m} + e^{s_h - m}.
+        // No real-token mass (no visible key) leaves out = 0; any other
+        // denominator, NaN included, divides, so non-finite inputs propagate.
         const float lt = lsum + __builtin_amdgcn_exp2f(s2 - mu);
-        const float inv = lt > 0.0f ? __builtin_amdgcn_rcpf(lt) : 0.0f;
+        const float inv = lsum == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(lt);
         // out^T goes through the wave's K tile (free after the last S^T) so
         // that the stores are whole 256-byte rows, 16 bytes per lane.
 #pragma unroll
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
         }
         if (lse != nullptr && hl == 0 && col_ok)
             lse[((size_t)b * Hq + h) * T + t] =
-                lt > 0.0f ? (mu + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+                lt == 0.0f ? -INFINITY : (mu + __builtin_amdgcn_logf(lt)) * kLn2;
     } else {
         if (!col_ok) return;
         // partial record [split][b][h][t]: acc[D] (relative to m), then (m, l), log2 units
@@ -308,21 +317,24 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ p
     float M = s2;
     for (int i = 0; i < n_splits; ++i) M = fmaxf(M, base[i * stride + D]);
     const float Mu = (M == -INFINITY) ? 0.0f : M;
-    float l = __builtin_amdgcn_exp2f(s2 - Mu);
+    float lreal = 0.0f;                         // real-token mass
     float acc0 = 0.0f, acc1 = 0.0f;
     for (int i = 0; i < n_splits; ++i) {
         const float *p = base + i * stride;
+        // a split that saw nothing has l = 0 (and m = -inf): weight 0; a NaN
+        // l also gets weight 0 and still turns the sums into NaN
         const float w = p[D + 1] > 0.0f ? __builtin_amdgcn_exp2f(p[D] - Mu) : 0.0f;
-        l += p[D + 1] * w;
+        lreal += p[D + 1] * w;
         acc0 += p[lane] * w;
         if (D > 64) acc1 += p[lane + 64] * w;
     }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float l = lreal + __builtin_amdgcn_exp2f(s2 - Mu);
+    const float inv = lreal == 0.0f ? 0.0f : 1.0f / l;
     bf16 *orow = out + (((size_t)b * T + t) * Hq + h) * D;
     orow[lane] = (bf16)(acc0 * inv);
     if (D > 64) orow[lane + 64] = (bf16)(acc1 * inv);
     if (lse != nullptr && lane == 0)
-        lse[((size_t)b * Hq + h) * T + t] = l > 0.0f ? (Mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+        lse[((size_t)b * Hq + h) * T + t] = l == 0.0f ? -INFINITY : (Mu + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
 int waves_to_groups(long items) { return (int)((items + kWavesPerWG - 1) / kWavesPerWG); }

@@ -93,15 +93,17 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     M = fmaxf(M, s2);
     const float Mu = (M == -INFINITY) ? 0.0f : M;
     const float f = exp2f(m - Mu);
-    float Ltot = l * f;
+    float Lreal = l * f;                               // real-token mass
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) Ltot += __shfl_xor(Ltot, off);
-    Ltot += exp2f(s2 - Mu);
+    for (int off = 32; off > 0; off >>= 1) Lreal += __shfl_xor(Lreal, off);
+    const float Ltot = Lreal + exp2f(s2 - Mu);
 #pragma unroll
     for (int d = 0; d < D; ++d) red[lane][d] = acc[d] * f;
     wts[lane] = 0.0f;
     __syncthreads();
-    const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+    // No real-token mass leaves out = 0; every other denominator divides (a
+    // NaN one included, so non-finite inputs propagate).
+    const float inv = Lreal == 0.0f ? 0.0f : 1.0f / Ltot;
     for (int d = lane; d < D; d += 64) {
         float s = 0.0f;
         for (int i = 0; i < 64; ++i) s += red[i][d];
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(64) void generic_f32_kernel(
     }
     if (lse != nullptr && lane == 0)
         lse[(!RING && cu != nullptr ? (size_t)h * total + q_row0 : ((size_t)b * Hq + h) * rows) + row] =
-            Ltot > 0.0f ? (Mu + log2f(Ltot)) * kLn2 : -INFINITY;
+            Ltot == 0.0f ? -INFINITY : (Mu + log2f(Ltot)) * kLn2;
 }
 
 template <int D>

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
         sn[tid] = (float)sin(a);
     }
     __syncthreads();
-    const int slot = (int)(P % R);
+    // Non-negative for any P, so a malformed (negative) cache_len_old still
+    // lands inside this sequence's ring.
+    const int slot = (int)(((P % R) + R) % R);
     const int nq = Hq * CH, nk = Hkv * CH, nv = Hkv * 2 * CH;
     for (int it = tid; it < nq + nk + nv; it += blockDim.x) {
         if (it < nq + nk) {

@@ -306,9 +306,12 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
 
         // Sink joins the denominator once: l_total = sum_j e^{x_j - m} + e^{s_h - m}.
         const float mu = (m == -INFINITY) ? 0.0f : m;
-        const float lt = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
+        const float lreal = wave_xor32_sum(l);
+        const float lt = lreal + __builtin_amdgcn_exp2f(s2 - mu);
         if (row_ok) {
-            const float inv = lt > 0.0f ? __builtin_amdgcn_rcpf(lt) : 0.0f;
+            // No real-token mass leaves out = 0; every other denominator
+            // divides (a NaN one included, so non-finite inputs propagate).
+            const float inv = lreal == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(lt);
             bf16 *orow = out + ((q_row0 + i) * Hq + h) * D;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             }
             if (lse != nullptr && hl == 0)
                 lse[(cu != nullptr ? (size_t)h * total + q_row0 : ((size_t)b * Hq + h) * S_q) + i] =
-                    lt > 0.0f ? (mu + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+                    lt == 0.0f ? -INFINITY : (mu + __builtin_amdgcn_logf(lt)) * kLn2;
         }
     }
 }

@@ -301,13 +301,16 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 
         // The sink joins the denominator once: l = sum_j e^{x_j - m} + e^{s_h - m}.
         const float mu = (m == -INFINITY) ? 0.0f : m;
-        l = wave_xor32_sum(l) + __builtin_amdgcn_exp2f(s2 - mu);
+        const float lreal = wave_xor32_sum(l);
+        l = lreal + __builtin_amdgcn_exp2f(s2 - mu);
         // Epilogue: out = O / l in bf16 (RNE), transposed through this wave's
         // LDS staging area 64 dims at a time and stored as full 128-byte row
         // segments; rows past the window are dropped by the hardware.  The
         // staging writes are issued while the last PV products may still be
         // running, so their data registers are held until they complete.
-        const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+        // No real-token mass leaves out = 0; every other denominator divides
+        // (a NaN one included, so non-finite inputs propagate).
+        const float inv = lreal == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(l);
         const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;
         bf16 (*stg)[64 + 8] = sm.ostage[wave];
 #pragma unroll
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
                 buf_store16_nt(x[i], orr, (8 * i + (lane >> 3)) * qrow_bytes + 128 * half + 16 * ch, so);
             asm volatile("" ::: "memory");             // next half's writes after these reads
         }
-        buf_store_f32(l > 0.0f ? (mu + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY, lr, l_lane,
+        buf_store_f32(l == 0.0f ? -INFINITY : (mu + __builtin_amdgcn_logf(l)) * kLn2, lr, l_lane,
                       (uint32_t)(p0 - c0) * 4);
 
         if (p0 + kTile < c1) st.store(sm, (T1 + 1) % R, tid);

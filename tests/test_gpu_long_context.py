@@ -39,6 +39,30 @@ def test_swa_prefill_262144_sampled_rows(gpu):
     check_lse(lse[0].index_select(1, idx).T, ref_lse, torch.bfloat16)
 
 
+def test_swa_prefill_65536_chunk_boundaries(gpu):
+    """The sliding-window layer of the hybrid 5:1 stack at full size
+    (S=65536, Hq=64, Hkv=8, D=128, window 128) in the launch the benchmark
+    times: the prefill then runs 2048-position chunks, each starting with its
+    own 127-key halo.  Rows around every chunk boundary (c-1, c, c+1, c+31,
+    c+32, c+126, c+127, c+128), the first and last 128 rows and 1024 seeded
+    random rows, all 64 heads."""
+    B, S, Hq, Hkv, D, W = 1, 65536, 64, 8, 128, 128
+    print("prefill 65536", flush=True)
+    q, k, v, sink = inputs.attention_inputs(4, 1, B, S, S, Hq, Hkv, D, torch.bfloat16, gpu)
+    out, lse = swa.swa_sink_prefill(q, k, v, sink, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4001)
+    edge = {c + d for c in range(0, S, 2048) for d in (-1, 0, 1, 31, 32, 126, 127, 128)}
+    rows = np.array(sorted({r for r in edge if 0 <= r < S} | set(range(128))
+                           | set(range(S - 128, S)) | set(rng.integers(0, S, 1024).tolist())))
+    idx = torch.as_tensor(rows, device=gpu)
+    ref_out, ref_lse = oracle.swa_prefill_rows(to64(q[0].index_select(0, idx)),
+                                               np.zeros(len(rows)), rows, to64(k), to64(v),
+                                               to64(sink), W)
+    check_out(out[0].index_select(0, idx), ref_out, torch.bfloat16)
+    check_lse(lse[0].index_select(1, idx).T, ref_lse, torch.bfloat16)
+
+
 @pytest.mark.parametrize("seq", [0, 7])
 def test_global_decode_262144_one_sequence(gpu, seq):
     """One of the 8 sequences in full (all 64 heads), as the bench launches it."""
