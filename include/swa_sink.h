@@ -30,8 +30,10 @@
  *    device pointer.
  *  - The caller owns and allocates every buffer; the library never
  *    allocates, frees or synchronises, keeps no mutable global state and is
- *    re-entrant.  Work is enqueued on `stream` (a hipStream_t; NULL = the
- *    default stream) and results are valid once the caller synchronises it.
+ *    re-entrant (except global_sink_attn_noalloc, which uses the library's
+ *    own static scratch array: see there).  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and results are valid once
+ *    the caller synchronises it.
  *  - Every argument is validated before any HIP call; a non-zero return
  *    means nothing was launched (SWA_ERR_HIP: the launch itself failed).
  *    Batch and row counts (B, S, T_q, S_q) may be 0: nothing is launched
@@ -78,7 +80,9 @@ enum swa_status {
     SWA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, unknown dtype, misaligned pointer,
                                  or window*D*2 > 2^31-1 bytes for one decode ring  */
     SWA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
-    SWA_ERR_HIP = -5          /* the HIP runtime reported an error at launch       */
+    SWA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch       */
+    SWA_ERR_SCRATCH = -6      /* global_sink_attn_noalloc: the sizes need more than
+                                 its static scratch array holds (64 MiB)           */
 };
 
 /*
@@ -224,6 +228,26 @@ SWA_API int global_sink_attn(const void *q, const void *k, const void *v, const 
                      void *out, float *lse, int B, int Hq, int Hkv, int S_q, int S_kv,
                      int D, void *workspace, size_t workspace_bytes, int dtype,
                      void *stream);
+
+/*
+ * global_sink_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results, with no workspace argument.
+ * Where global_sink_attn would use a workspace (short query blocks split over
+ * the keys), the partial results go to a static device array of the library
+ * instead, 64 MiB per GPU, held from the first such call on that GPU until
+ * the process ends.  Sizes whose
+ * global_sink_attn_workspace_bytes(...) exceeds 64 MiB return
+ * SWA_ERR_SCRATCH before anything is launched.  The call itself allocates
+ * nothing (no hipMalloc, no library allocation); its first call on a device
+ * looks up that device's copy of the array.  Calls that overlap on one GPU
+ * (several streams or threads) share the array and race: serialise them.
+ * Each call's partials are written before they are read, so successive calls
+ * need no clearing.
+ */
+SWA_API int global_sink_attn_noalloc(const void *q, const void *k, const void *v,
+                                     const float *sink, void *out, float *lse, int B, int Hq,
+                                     int Hkv, int S_q, int S_kv, int D, int dtype, void *stream);
 
 /*
  * global_sink_attn plus a block-score side output: for every query head h,

@@ -25,6 +25,7 @@ __all__ = [
     "swa_sink_rope_append",
     "global_sink_attn",
     "global_sink_attn_workspace_bytes",
+    "global_sink_attn_noalloc",
     "global_sink_attn_block_max",
     "swa_sink_backward",
     "swa_sink_backward_workspace_bytes",
@@ -254,6 +255,31 @@ def global_sink_attn(q, k, v, sink, out=None, lse=None, workspace=None, want_lse
     _call(_lib.load().global_sink_attn, "global_sink_attn", _ptr(q), _ptr(k), _ptr(v),
           _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, D, _ptr(workspace), wbytes,
           dt, _stream(stream))
+    return out, lse
+
+
+def global_sink_attn_noalloc(q, k, v, sink, out=None, lse=None, want_lse: bool = True,
+                             stream=None):
+    """global_sink_attn without a workspace: the library's static per-GPU
+    scratch array holds the split partials (64 MiB; larger sizes raise).
+    Calls overlapping on one GPU race on that array.  Outputs are allocated
+    here when not given; the C call itself allocates nothing."""
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Skv, Hkv, D) or v.shape != k.shape or sink.shape != (Hq,):
+        raise ValueError("shape mismatch")
+    _float32_sink(sink)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Sq), torch.float32, "lse")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), device=q.device, dtype=torch.float32)
+    _check_device(q, k, v, sink, out, lse)
+    dt = _dtype_code(q, k, v, out)
+    _call(_lib.load().global_sink_attn_noalloc, "global_sink_attn_noalloc", _ptr(q), _ptr(k),
+          _ptr(v), _ptr(sink), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Skv, D, dt,
+          _stream(stream))
     return out, lse
 
 

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa_sink
 SWA_F32, SWA_BF16 = 0, 1
 SWA_OK = 0
 SWA_ERR_NULL, SWA_ERR_SHAPE, SWA_ERR_UNSUPPORTED, SWA_ERR_WORKSPACE, SWA_ERR_HIP = -1, -2, -3, -4, -5
+SWA_ERR_SCRATCH = -6
 
 EXPORTS = (
     "swa_sink_prefill",
@@ -22,6 +23,7 @@ EXPORTS = (
     "swa_sink_rope_append",
     "global_sink_attn_workspace_bytes",
     "global_sink_attn",
+    "global_sink_attn_noalloc",
     "global_sink_attn_block_max",
     "swa_sink_backward_workspace_bytes",
     "swa_sink_backward",
@@ -59,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.global_sink_attn_workspace_bytes.restype = sz
     lib.global_sink_attn.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, sz, i, vp]
     lib.global_sink_attn.restype = i
+    lib.global_sink_attn_noalloc.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, i, vp]
+    lib.global_sink_attn_noalloc.restype = i
     lib.global_sink_attn_block_max.argtypes = [vp, vp, vp, fp, vp, fp, fp, i, i, i, i, i, i, i,
                                                i, vp]
     lib.global_sink_attn_block_max.restype = i

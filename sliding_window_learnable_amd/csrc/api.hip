@@ -174,6 +174,30 @@ int global_sink_attn(const void *q, const void *k, const void *v, const float *s
     return status_of(swa::launch_stream_bf16(a, st));
 }
 
+int global_sink_attn_noalloc(const void *q, const void *k, const void *v, const float *sink,
+                             void *out, float *lse, int B, int Hq, int Hkv, int S_q, int S_kv,
+                             int D, int dtype, void *stream) {
+    if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
+    if (S_q < 0 || S_kv < 0 || S_q > S_kv) return SWA_ERR_SHAPE;
+    const int rc = common_checks(B, Hq, Hkv, D, dtype);
+    if (rc != SWA_OK) return rc;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(sink, 4) || !aligned(lse, 4))
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S_q == 0) return SWA_OK;
+    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+
+    swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SWA_F32) return status_of(swa::launch_generic_f32_linear(a, st));
+    if (swa::splitkv_preferred(Hq, Hkv, S_q, S_kv)) {
+        if (swa::splitkv_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D) > swa::kStaticScratchBytes)
+            return SWA_ERR_SCRATCH;
+        return status_of(swa::launch_splitkv_bf16_static(a, st));
+    }
+    return status_of(swa::launch_stream_bf16(a, st));
+}
+
 int global_sink_attn_block_max(const void *q, const void *k, const void *v, const float *sink,
                                void *out, float *lse, float *block_max, int block_k, int B,
                                int Hq, int Hkv, int S_q, int S_kv, int D, int dtype,
@@ -240,6 +264,9 @@ const char *swa_sink_strerror(int code) {
                "aligned to 16 bytes, or a ring cache above 2 GiB per (sequence, KV head))";
     case SWA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case SWA_ERR_HIP: return "the HIP runtime reported an error when launching";
+    case SWA_ERR_SCRATCH:
+        return "the sizes need more scratch than the static 64 MiB array of "
+               "global_sink_attn_noalloc holds";
     default: return "unknown status code";
     }
 }

@@ -16,6 +16,8 @@
 // tokens.  Decode is bound by HBM: every wave streams its own keys with the
 // next chunk's loads in flight while the current chunk computes, and waves
 // never wait on each other, so each CU keeps ~16 KiB per wave in flight.
+#include <mutex>
+
 #include "attn_device.h"
 #include "launch.h"
 
@@ -414,6 +416,49 @@ size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D)
 
 hipError_t launch_splitkv_bf16(const PrefillArgs &a, void *workspace, hipStream_t stream) {
     return a.D == 64 ? splitkv_d<64>(a, workspace, stream) : splitkv_d<128>(a, workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the split-KV partials go to a static device array
+// instead of a caller workspace.  Each GPU holds its own copy of `scratch`
+// for the life of the process; host code only ever passes the device address
+// found by hipGetSymbolAddress (once per device, with that device current).
+// Every record the combine pass reads is written by the partial pass of the
+// same call, so nothing in it has to start at zero.  Calls that overlap on
+// one GPU (several streams or host threads) share the array and race.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_splitkv_bf16_static(const PrefillArgs &a, hipStream_t stream) {
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_splitkv_bf16(a, ws, stream);
 }
 
 }  // namespace swa

@@ -65,6 +65,10 @@ int splitkv_num_splits(int B, int Hq, int Hkv, int S_q, int S_kv);
 bool splitkv_preferred(int Hq, int Hkv, int S_q, int S_kv);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
 hipError_t launch_splitkv_bf16(const PrefillArgs &a, void *workspace, hipStream_t stream);
+// The same with the partials in the library's static per-device scratch
+// array (kStaticScratchBytes); the caller checks the size first.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t launch_splitkv_bf16_static(const PrefillArgs &a, hipStream_t stream);
 
 // Backward of causal sliding-window / global attention with a sink.
 struct BackwardArgs {

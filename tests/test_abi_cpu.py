@@ -43,14 +43,15 @@ def test_status_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("SWA_OK", 0), ("SWA_ERR_NULL", -1), ("SWA_ERR_SHAPE", -2),
                       ("SWA_ERR_UNSUPPORTED", -3), ("SWA_ERR_WORKSPACE", -4),
-                      ("SWA_ERR_HIP", -5), ("SWA_F32", 0), ("SWA_BF16", 1)]:
+                      ("SWA_ERR_HIP", -5), ("SWA_ERR_SCRATCH", -6), ("SWA_F32", 0),
+                      ("SWA_BF16", 1)]:
         assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text), name
         assert getattr(_lib, name) == val
 
 
 def test_strerror_every_code(lib):
     seen = set()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = lib.swa_sink_strerror(code).decode()
         assert s and s not in seen
         seen.add(s)
@@ -311,3 +312,22 @@ def test_prefill_varlen_empty_is_noop(lib):
     assert pvar(lib, B=0) == _lib.SWA_OK
     assert pvar(lib, S=0) == _lib.SWA_OK
     assert pvar(lib, total=0) == _lib.SWA_OK
+
+
+def test_noalloc_rejects_sizes_beyond_its_static_scratch(lib):
+    """global_sink_attn_noalloc checks the split partials' size against its
+    64 MiB static array before any HIP call: 4096 single-token rows of 64
+    heads need 4096 * 64 * 130 * 4 bytes (136 MB).  Argument errors come
+    first, as in global_sink_attn."""
+    f = lib.global_sink_attn_noalloc
+    need = lib.global_sink_attn_workspace_bytes(4096, 64, 8, 1, 65536, 128)
+    assert need > 64 << 20
+    assert f(P, P, P, P, P, P, 4096, 64, 8, 1, 65536, 128, _lib.SWA_BF16, None) == \
+        _lib.SWA_ERR_SCRATCH
+    assert f(None, P, P, P, P, P, 4096, 64, 8, 1, 65536, 128, 1, None) == _lib.SWA_ERR_NULL
+    assert f(P, P, P, P, P, P, 4, 64, 8, 2, 1, 128, 1, None) == _lib.SWA_ERR_SHAPE
+    assert f(P, P, P, P, P, P, 4, 64, 8, 1, 10, 96, 1, None) == _lib.SWA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, P, P, 0, 64, 8, 1, 10, 128, 1, None) == _lib.SWA_OK
+    # just inside the limit: the size is accepted (nothing launched here:
+    # validation only, the sizes are checked against the workspace formula)
+    assert lib.global_sink_attn_workspace_bytes(8, 64, 8, 4, 262144, 128) <= 64 << 20
