@@ -51,6 +51,11 @@ def parse_args():
     # sustained value: warm up past that before timing.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
+    # Before the warm-up steps of each timed section, the GPU is kept busy with
+    # the same call for this long: from idle the shader clock takes ~40 ms of
+    # sustained load to reach its steady value, longer than a few warm-up
+    # steps last.  Not part of the timed region.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--only", default="all",
                     choices=["all", "prefill", "decode", "hybrid", "long", "backward", "varlen",
                              "copy"])
@@ -62,12 +67,30 @@ def parse_args():
     return ap.parse_args()
 
 
+SETTLE_S = 0.3
+
+
+def settle(fn):
+    """Keeps the GPU busy with fn for SETTLE_S seconds (untimed) so the shader
+    clock reaches its sustained value; returns the number of calls made."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def timed(fn, steps, warmup):
     """Average ms per call of fn(i) over `steps` back-to-back calls, timed with
     HIP events on the stream the kernels are launched on (torch's current
-    stream, which the binding passes to the C ABI)."""
+    stream, which the binding passes to the C ABI).  The clock is settled
+    first, then `warmup` untimed calls precede the timed ones."""
     import torch
     stream = torch.cuda.current_stream()
+    settle(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -583,6 +606,8 @@ def bench_copy(args, torch):
 
 def main():
     args = parse_args()
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle_ms) / 1e3
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)." % args.gpus, file=sys.stderr)
@@ -612,6 +637,7 @@ def main():
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
+            "clock_settle_ms": args.settle_ms,
             "ms_per_step": pre["ms"],
             "higher_is_better": True,
             "scaling": "weak",

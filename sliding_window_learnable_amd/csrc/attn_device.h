@@ -113,6 +113,25 @@ __device__ __forceinline__ void lds_settle(const V (&w)[N]) {
         asm volatile("s_waitcnt lgkmcnt(0)" : : "v"(w[0]) : "memory");
 }
 
+// Waits until at most N vector memory operations of this wave are
+// outstanding, holding the registers in w until then: the data registers
+// of earlier 16-byte stores, which the store may read after the
+// instructions that follow it (the compiler treats them as free once the
+// store has issued).  N counts the operations issued after those stores.
+template <int N, class V, int K>
+__device__ __forceinline__ void hold_until_done(const V (&w)[K]) {
+    static_assert(K == 4 || K == 8, "hold_until_done holds 4 or 8 registers");
+    if constexpr (K == 8)
+        asm volatile("s_waitcnt vmcnt(%8)"
+                     :
+                     : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]),
+                       "v"(w[6]), "v"(w[7]), "n"(N)
+                     : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%4)" : : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "n"(N)
+                     : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Buffer addressing.  A 128-bit resource (base, byte range) lives in SGPRs,
 // each lane supplies one 32-bit byte offset, uniform offsets go in an SGPR.
@@ -200,6 +219,15 @@ __device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
     const unsigned la = __builtin_amdgcn_readfirstlane(
         (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(la),
+                 "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+// The same copy with the non-temporal cache policy, for data read exactly
+// once in whole cache lines per instruction.
+__device__ __forceinline__ void dma16_nt(u32x4 r, const void *lds, uint32_t voff) {
+    const unsigned la = __builtin_amdgcn_readfirstlane(
+        (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(la),
                  "v"(voff), "s"(r)
                  : "memory", "m0");
 }

@@ -11,20 +11,33 @@
 //  * the G query heads that share a KV head are served by the waves of one
 //    work-group, so every K/V byte staged in LDS is used by all G heads;
 //  * the chunk is walked in steps of 32 query positions; a step needs the
-//    key tiles T1-ntw+1 .. T1 (32 keys each, T1 = the step's own tile), which
-//    live in an LDS ring of ntw+1 tiles -- each step loads ONE new tile
-//    (prefetched into registers while the current step computes), so K and
-//    V cross HBM about once plus a (window-1)-key halo per chunk;
-//  * per wave and head: S^T = K Q^T on bf16 MFMA for all ntw tiles at once,
-//    band mask, one softmax pass seeded with the sink (running max starts at
-//    s_h, denominator at exp(s_h - max)), O^T = V^T P^T on MFMA, then
-//    out = O / l (bf16, RNE) and lse = max + ln l.
+//    key tiles T1-4 .. T1 (32 keys each, T1 = the step's own tile), which
+//    live in an LDS ring of six tiles -- each step copies ONE new tile, so
+//    K and V cross HBM about once plus a (window-1)-key halo per chunk;
+//  * per wave and head: S^T = K Q^T on bf16 MFMA tile by tile, band mask on
+//    the edge tiles, online softmax seeded with the sink (running max starts
+//    at s_h, denominator gets exp(s_h - max) once), O^T = V^T P^T on MFMA,
+//    then out = O / l (bf16, RNE) and lse = max + ln l.
 //  * packed batches of sequences of different lengths (serving mixed
 //    context lengths together: "小米罗福莉：MiMo-V2.5如何做到又快又强又便宜？|
 //    ICML 2026", §06 Q&A) use the same step code: the concatenation of every
 //    sequence's 32-row tiles is split evenly over the work-groups, and a
 //    work-group runs one segment per sequence its share meets, each segment
 //    starting with its own (window-1)-key halo.
+//
+// Memory path: every input reaches LDS by buffer->LDS copies (no staging
+// registers): the K and V tiles into the ring, each wave's next 32 query
+// rows into its own Q tile, one step ahead (the query rows are read once, in
+// whole rows per instruction, so their copies are non-temporal).  All tiles
+// are unpadded rows whose 16-byte chunks are XOR-swizzled by row, so the K
+// and Q fragment reads and the transposing V reads are free of bank
+// conflicts.  Once a step's products are issued, the wave moves the next
+// step's Q fragments into registers and its Q tile becomes the output
+// staging area: the rows of the P.V products are fed dims in the same
+// permuted order as the score rows are fed keys, so each lane holds 8
+// consecutive dims per register half and writes them as one 16-byte chunk;
+// the rows are read back whole and stored as full 256-byte rows per 16
+// lanes with non-temporal stores (written once, whole lines reach HBM).
 #include "attn_device.h"
 #include "launch.h"
 
@@ -33,71 +46,13 @@ namespace {
 
 constexpr int kTile = 32;
 constexpr int kMaxTiles = 5;             // ceil((129-1)/32) + 1
-constexpr int kRing = kMaxTiles + 1;     // + the tile being prefetched
-constexpr int kRingKeys = kRing * kTile;
+constexpr int kRing = kMaxTiles + 1;     // + the tile being copied
 
 template <int D, int NW>
 struct RingSmem {
-    bf16 k[kRing][kTile][D + 8];
-    bf16 vt[D][kRingKeys + 8];
-    // Per-wave output staging: 32 queries x 64 dims (half of D = 128 at a
-    // time), so that global stores are whole 128-byte row segments.
-    bf16 ostage[NW][kTile][64 + 8];
-};
-
-// Stages one 32-key tile: K rows as 16-byte chunks into sm.k[slot], V as
-// 4-key x 8-dim quads written transposed into sm.vt.  The global loads go
-// into registers at the start of a step and reach LDS at its end.
-template <int D, int NT>
-struct Stager {
-    static constexpr int CH = D / 8;                       // 16-byte chunks per row
-    static constexpr int KPT = (kTile * CH + NT - 1) / NT; // K chunks per thread
-    static constexpr int VPT = (8 * CH + NT - 1) / NT;     // V quads per thread
-    bf16x8 kreg[KPT];
-    bf16x8 vreg[VPT][4];
-
-    // Rows past the end of the descriptor's range read as zeros.
-    __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, uint32_t rs, uint32_t row0,
-                                         int tid) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int item = min(tid + i * NT, kTile * CH - 1);
-            kreg[i] = buf_load16(kr, (item / CH) * rs + 16 * (item % CH), row0 * rs);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int item = min(tid + i * NT, 8 * CH - 1);
-            const uint32_t vo = 4 * (item & 7) * rs + 16 * (item >> 3);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vreg[i][j] = buf_load16(vr, vo, (row0 + j) * rs);
-        }
-    }
-
-    template <class Smem>
-    __device__ __forceinline__ void store(Smem &sm, int slot, int tid) const {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < kTile * CH)
-                *(bf16x8 *)&sm.k[slot][item / CH][8 * (item % CH)] = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int item = tid + i * NT;
-            if (item < 8 * CH) {
-                const int kq = item & 7, ch = item >> 3;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16x4 w;
-                    w[0] = vreg[i][0][e];
-                    w[1] = vreg[i][1][e];
-                    w[2] = vreg[i][2][e];
-                    w[3] = vreg[i][3][e];
-                    *(bf16x4 *)&sm.vt[8 * ch + e][slot * kTile + 4 * kq] = w;
-                }
-            }
-        }
-    }
+    bf16 k[kRing][kTile][D];             // K rows, chunks swizzled by row
+    bf16 v[kRing][kTile][D];             // V rows, chunks swizzled by row
+    bf16 q[NW][kTile][D];                // each wave's next 32 query rows, swizzled
 };
 
 // One work-group = (batch, KV head g, chunk of positions); wave w serves
@@ -109,21 +64,29 @@ struct Stager {
 // rescaled), P packed to bf16, O^T += V^T P^T (MFMA).  The sink adds
 // exp(s_h - max) to the denominator once at the end.
 //
-// Memory pipeline per wave: Q fragments are double-buffered (the loads for
-// step n+1 are issued when step n starts), the next step's K/V tile is
-// loaded into registers at the start of a step and written into the free
-// ring slot at its end, and output stores are never waited on.  Every
-// global access is a buffer access relative to this work-group's window of
-// the tensor, so rows past the end need no special code.
+// Per step n, each wave: passes the work-group barrier (tile T1 is whole --
+// every wave waited for its share at the end of step n-1 -- and every wave
+// is done with the slot tile T1+1 goes to), starts the copies of tile T1+1
+// and of its Q tile for step n+1, computes with the Q fragments of step n,
+// waits for those copies, takes the step n+1 fragments into registers,
+// stages and stores its output rows.  Every global access is a buffer access relative
+// to this work-group's window of the tensor, so rows past the end need no
+// special code (loads return zeros, stores are dropped).
 template <int D, int NW, bool PACKED>
 __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse, int S,
     int Hq, int Hkv, int W, int ntw, int chunk, const int32_t *__restrict__ cu, int B,
     int total) {
-    constexpr int NT = NW * 64;
     constexpr float kSlack = 8.0f;                               // log2 units
     constexpr float kBig = 256.0f;                               // 2^kSlack
+    constexpr int CPR = D / 8;                                   // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                                // rows per copy instruction
+    constexpr int NI = 2 * kTile / RPI;                          // copies per K+V tile
+    constexpr int IPW = NI / NW;                                 // ... per wave
+    constexpr int QI = kTile / RPI;                              // copies per Q tile
+    constexpr int NST = 2 * (D / 32) + 1;                        // stores per step (out, lse)
+    static_assert(IPW >= 1 && IPW * NW == NI, "copy split");
     __shared__ __align__(16) RingSmem<D, NW> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -141,45 +104,75 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 
     // The segment being computed: positions [c0, c1) of one sequence.
     // Buffer windows: q/out rows [c0, c1) (all heads); k/v rows [r0, c1) of
-    // KV head g -- every row the segment uses (the prefetch past its last
-    // tile reads zeros and is never stored); the lse entries of head h.
+    // KV head g -- every row the segment uses (the copy past its last tile
+    // reads zeros and is never used); the lse entries of head h.
     int c0 = 0, c1 = 0, r0 = 0;
-    rsrc_t qr, orr, kr, vr, lr;
-    // QK contraction order: lane half hl feeds dims [64hl, 64hl + 64), the
-    // ks-th MFMA step dims 64hl + 8ks .. +8, so each lane reads one whole
-    // 128-byte line of its query row (K fragments use the same order).
-    const uint32_t q_lane = lq * qrow_bytes + D * hl;              // + 16*ks
+    u32x4 qd, kd, vd;
+    rsrc_t orr, lr;
     const uint32_t l_lane = hl == 0 ? 4u * lq : kOutOfRange;       // one lane per query
     const float s2 = sink[h] * kLog2e;
 
-    auto load_q = [&](bf16x8 (&qf)[D / 16], int p0) {
-        const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;    // past the window: zeros
+    // Copy geometry.  K/V: instruction u of this wave moves RPI rows of the
+    // K (first half of the instructions) or V tile; Q: instruction u moves
+    // rows RPI*u .. of this wave's 32 query rows.  Lane l's 16 bytes land at
+    // 16*l past the instruction's first row: row l / CPR, chunk position
+    // l % CPR, which holds source chunk (l % CPR) ^ swz(row).
+    uint32_t kv_off[IPW];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = buf_load16(qr, q_lane + 16 * ks, so);
-    };
-
-    Stager<D, NT> st;
-
-    // S^T of one tile: 32 keys of ring slot `slot` x this wave's 32 queries.
-    auto qk = [&](const bf16x8 (&cur)[D / 16], int slot) {
-        const bf16 *krow = &sm.k[slot][score_row_key(lq)][(D / 2) * hl];
-        f32x16 sc = mfma32(*(const bf16x8 *)krow, cur[0], zero16());
+    for (int u = 0; u < IPW; ++u) {
+        const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
+        kv_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
+    }
+    uint32_t q_off[QI];
 #pragma unroll
-        for (int ks = 1; ks < D / 16; ++ks)
-            sc = mfma32(*(const bf16x8 *)(krow + 8 * ks), cur[ks], sc);
-        return sc;
-    };
-    // Band mask of a tile starting rel keys after the step's first query.
-    auto band = [&](f32x16 &sc, int rel) {
+    for (int u = 0; u < QI; ++u) {
+        const int row = RPI * u + lane / CPR;
+        q_off[u] = row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row));
+    }
+    // Tile T into its ring slot (rows from r0; past the window: zeros).
+    auto copy_kv = [&](int T) {
+        const uint32_t to = (uint32_t)(kTile * T - r0) * rs;
+        const int slot = T % R;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int dk = 16 * (r >> 3) + (r & 7) + kbias + rel;
-            sc[r] = (dk <= 0 && dk > -W) ? sc[r] : -INFINITY;
+        for (int u = 0; u < IPW; ++u) {
+            const int ii = wave * IPW + u;                       // uniform
+            const bool is_k = ii < NI / 2;
+            bf16(*tile)[D] = is_k ? sm.k[slot] : sm.v[slot];
+            dma16(is_k ? kd : vd, tile[(ii % (NI / 2)) * RPI], kv_off[u] + to);
         }
     };
-    // One-sided masks for the steady state: the newest tile only needs
-    // key <= query, older tiles only key > query - W (kr <= -kbias and
-    // kr > -W - kbias - rel respectively, kr being a per-register constant).
+    // The 32 query rows from position p into this wave's Q tile.
+    auto copy_q = [&](int p) {
+        const uint32_t to = (uint32_t)(p - c0) * qrow_bytes;
+#pragma unroll
+        for (int u = 0; u < QI; ++u) dma16_nt(qd, sm.q[wave][RPI * u], q_off[u] + to);
+    };
+
+    // QK contraction order: lane half hl feeds dims [D/2*hl, D/2*hl + D/2),
+    // the ks-th MFMA step the 16-byte chunk (D/16)*hl + ks -- for the Q
+    // fragments (B operand) and the K rows (A operand) alike.
+    const int arow = score_row_key(lq);
+    const int arow_s = swz<D>(arow), qrow_s = swz<D>(lq);
+    auto read_q = [&](bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qf[ks] = *(const bf16x8 *)&sm.q[wave][lq][8 * (((D / 16) * hl + ks) ^ qrow_s)];
+    };
+    // S^T of one tile: 32 keys of ring slot `slot` x this wave's 32 queries.
+    auto qk = [&](const bf16x8 (&cur)[D / 16], int slot) {
+        const bf16 *krow = sm.k[slot][arow];
+        bf16x8 a[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            a[ks] = *(const bf16x8 *)(krow + 8 * (((D / 16) * hl + ks) ^ arow_s));
+        f32x16 sc = mfma32(a[0], cur[0], zero16());
+#pragma unroll
+        for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], cur[ks], sc);
+        return sc;
+    };
+    // One-sided masks: the newest tile only needs key <= query, the oldest
+    // ones key > query - W (kr <= -kbias and kr > -W - kbias - rel
+    // respectively, kr being a per-register constant).
     auto causal = [&](f32x16 &sc) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -237,31 +230,61 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         p0b = pack8(p, 0);
         p1b = pack8(p, 1);
     };
-    auto pv = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot) {
-        const int col = slot * kTile + 8 * hl;
+    // O^T += V^T P^T.  A row m of a 32-dim tile is dim 32dt + score_row_key(m)
+    // (the score rows' permutation), so accumulator register r of lane l
+    // holds dim 32dt + 16(r>>3) + 8(l>>5) + (r&7): eight consecutive dims per
+    // register half.  The A operand comes from the V row tile by transposing
+    // reads: in each 16-lane group lane j names 4 dims of key row j/4 --
+    // dims 4*pm(j&3) of the group's 16-dim span, pm = (0, 2, 1, 3), which is
+    // the permutation within 16 rows -- and lane i receives dim i of the 4 rows.
+    const int tr_j = lane & 15;
+    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (((tr_j & 1) << 1) | ((tr_j >> 1) & 1));
+    auto pv = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot,
+                  bool first) {
+        const bf16(*vt)[D] = sm.v[slot];
+        bf16x8 va[D / 32][2];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col], p0b, o[dt]);
-            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16], p1b, o[dt]);
+            const int d = 32 * dt + tr_d, cc = d >> 3, half = (d >> 2) & 1;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
+                const bf16x4 lo = lds_read_tr(&vt[r1][8 * (cc ^ swz<D>(r1)) + 4 * half]);
+                const bf16x4 hi4 = lds_read_tr(&vt[r2][8 * (cc ^ swz<D>(r2)) + 4 * half]);
+                va[dt][kk] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            o[dt] = mfma32(va[dt][0], p0b, first ? zero16() : o[dt]);
+            o[dt] = mfma32(va[dt][1], p1b, o[dt]);
         }
     };
 
-    auto pv_first = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot) {
-        const int col = slot * kTile + 8 * hl;
+    // Output rows of the previous step, as read back for its stores.  A
+    // 16-byte store can read its data registers after the instructions that
+    // follow it have already run (later than the compiler's hazard model
+    // allows), so these registers are held -- named by the wait that retires
+    // the stores -- until the stores are known complete, early in the next
+    // step.
+    bf16x8 xo[D / 16];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col], p0b, zero16());
-            o[dt] = mfma32(*(const bf16x8 *)&sm.vt[32 * dt + lq][col + 16], p1b, o[dt]);
-        }
-    };
+    for (int i = 0; i < D / 16; ++i) xo[i] = bf16x8{};
+    bf16x8 cur[D / 16];                  // Q fragments of the current step
 
-    // One 32-position step with Q fragments `cur`; refills `fill` with the Q
-    // of the next step.
-    auto step = [&](const bf16x8 (&cur)[D / 16], bf16x8 (&fill)[D / 16], int p0) {
+    // One 32-position step: Q of this step in `cur`, key tile T1 in the ring
+    // (copied during the previous step or the prologue).
+    auto step = [&](int p0) {
         const int T1 = p0 / kTile;
-        lds_barrier();                                           // ring slot T1 staged
-        st.load(kr, vr, rs, kTile * (T1 + 1) - r0, tid);         // next step's tile
-        load_q(fill, p0 + kTile);
+        // This wave's share of tile T1 landed before the end of step n-1;
+        // after the barrier the whole tile is there and every wave is done
+        // with the slot tile T1+1 goes to.
+        lds_barrier();
+        copy_kv(T1 + 1);                                         // next step's tile
+        copy_q(p0 + kTile);                                      // next step's queries
+        // The previous step's stores are complete (only this step's copies
+        // may be outstanding): their data registers may now be reused.
+        hold_until_done<IPW + QI>(xo);
 
         float m = s2;                                            // running max (log2 units)
         float l = 0.0f;                                          // this lane's share of sum
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         // tile t, the PV products of tile t before the mask/max of tile t+1.
         // Tile 0 needs the causal mask, tile 4 (and tile 3 when W < 128) the
         // window edge; in the first four steps of a sequence, tiles before
-        // position 0 read any resident slot and are masked out entirely.
+        // position 0 read the step's own slot and are masked out entirely.
         f32x16 s_cur = qk(cur, T1 % R);
         causal(s_cur);
         m = fmaxf(m, tile_max(s_cur));                           // nothing accumulated yet
@@ -284,10 +307,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             if (t + 1 < kMaxTiles) s_next = qk(cur, (T >= 1 ? T - 1 : T1) % R);
             bf16x8 pa, pbb;
             softmax_tile(s_cur, m, l, o, pa, pbb);
-            if (t == 0)
-                pv_first(o, pa, pbb, T1 % R);
-            else
-                pv(o, pa, pbb, (T >= 0 ? T : T1) % R);
+            pv(o, pa, pbb, (T >= 0 ? T : T1) % R, t == 0);
             if (t + 1 < kMaxTiles) {
                 if (T - 1 < 0) {
 #pragma unroll
@@ -299,48 +319,47 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             }
         }
 
+        // The next step's Q tile has landed (and this step's tile copies):
+        // its fragments replace this step's, whose products are all issued.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        read_q(cur);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // Q tile free for staging
+
         // The sink joins the denominator once: l = sum_j e^{x_j - m} + e^{s_h - m}.
         const float mu = (m == -INFINITY) ? 0.0f : m;
         const float lreal = wave_xor32_sum(l);
         l = lreal + __builtin_amdgcn_exp2f(s2 - mu);
-        // Epilogue: out = O / l in bf16 (RNE), transposed through this wave's
-        // LDS staging area 64 dims at a time and stored as full 128-byte row
-        // segments; rows past the window are dropped by the hardware.  The
-        // staging writes are issued while the last PV products may still be
-        // running, so their data registers are held until they complete.
         // No real-token mass leaves out = 0; every other denominator divides
         // (a NaN one included, so non-finite inputs propagate).
         const float inv = lreal == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(l);
+        // out = O / l in bf16 (RNE): each lane writes its two 8-dim chunks
+        // per 32-dim tile into the staging tile (row = its query), then
+        // every lane reads back one 16-byte chunk of whole rows and stores
+        // it; rows past the window are dropped by the buffer range.
         const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;
-        bf16 (*stg)[64 + 8] = sm.ostage[wave];
+        bf16(*stg)[D] = sm.q[wave];
+        {
+            bf16x8 w[D / 16];
 #pragma unroll
-        for (int half = 0; half < D / 64; ++half) {
-            u32x2 w[8];
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
+                for (int e = 0; e < 2; ++e) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    bf16x4 x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[2 * half + dd][4 * jj + e] * inv);
-                    w[4 * dd + jj] = __builtin_bit_cast(u32x2, x);
-                    *(u32x2 *)&stg[lq][32 * dd + 8 * jj + 4 * hl] = w[4 * dd + jj];
+                    for (int i = 0; i < 8; ++i) w[2 * dt + e][i] = (bf16)(o[dt][8 * e + i] * inv);
+                    const int ch = (32 * dt + 16 * e + 8 * hl) / 8;
+                    *(bf16x8 *)&stg[lq][8 * (ch ^ qrow_s)] = w[2 * dt + e];
                 }
-            }
             lds_settle(w);
-            const int ch = lane & 7;
-            bf16x8 x[kTile / 8];
+        }
 #pragma unroll
-            for (int i = 0; i < kTile / 8; ++i) x[i] = *(const bf16x8 *)&stg[8 * i + (lane >> 3)][8 * ch];
+        for (int u = 0; u < QI; ++u) xo[u] = *(const bf16x8 *)&stg[RPI * u + lane / CPR][8 * (lane % CPR)];
 #pragma unroll
-            for (int i = 0; i < kTile / 8; ++i)
-                buf_store16_nt(x[i], orr, (8 * i + (lane >> 3)) * qrow_bytes + 128 * half + 16 * ch, so);
-            asm volatile("" ::: "memory");             // next half's writes after these reads
+        for (int u = 0; u < QI; ++u) {
+            const int row = RPI * u + lane / CPR;
+            buf_store16_nt(xo[u], orr, row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row)), so);
         }
         buf_store_f32(l == 0.0f ? -INFINITY : (mu + __builtin_amdgcn_logf(l)) * kLn2, lr, l_lane,
                       (uint32_t)(p0 - c0) * 4);
-
-        if (p0 + kTile < c1) st.store(sm, (T1 + 1) % R, tid);
     };
 
     // Segments.  Uniform batch (!PACKED): one, the chunk [c0, c1) of
@@ -398,44 +417,34 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             c0 = kTile * max(t0 - excl, 0);
             c1 = min(kTile * min(t1 - excl, n), len);
             lrow = lse != nullptr ? lse + (size_t)h * total + row0 : nullptr;
-            if (!first) __syncthreads();   // the previous segment's last reads of the ring
+            // The previous segment's copies have landed and every wave is
+            // done reading its ring and Q tiles.
+            if (!first) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
         }
         first = false;
 
         const int T_first = max(0, c0 / kTile - ntw + 1);
         r0 = kTile * T_first;
-        qr = make_rsrc(q + ((row0 + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
+        qd = sgpr_rsrc(q + ((row0 + c0) * Hq + h) * D, (uint32_t)(c1 - c0) * qrow_bytes);
+        kd = sgpr_rsrc(k + ((row0 + r0) * Hkv + g) * D, (uint32_t)(c1 - r0) * rs);
+        vd = sgpr_rsrc(v + ((row0 + r0) * Hkv + g) * D, (uint32_t)(c1 - r0) * rs);
         orr = make_rsrc(out + ((row0 + c0) * Hq + h) * D, (c1 - c0) * qrow_bytes);
-        kr = make_rsrc(k + ((row0 + r0) * Hkv + g) * D, (c1 - r0) * rs);
-        vr = make_rsrc(v + ((row0 + r0) * Hkv + g) * D, (c1 - r0) * rs);
         lr = make_rsrc(lrow != nullptr ? lrow + c0 : nullptr,
                        lrow != nullptr ? (uint32_t)(c1 - c0) * 4 : 0u);
-        bf16x8 qa[D / 16], qb[D / 16];
-        if constexpr (!PACKED) {
-            // The first step's Q and every window tile up to the step's own
-            // are all requested before any is waited for.
-            load_q(qa, c0);
-            Stager<D, NT> pro[kMaxTiles];
-            const int n_pro = c0 / kTile - T_first + 1;   // <= ntw <= kMaxTiles
-#pragma unroll
-            for (int u = 0; u < kMaxTiles; ++u)
-                if (u < n_pro) pro[u].load(kr, vr, rs, kTile * (T_first + u) - r0, tid);
-#pragma unroll
-            for (int u = 0; u < kMaxTiles; ++u)
-                if (u < n_pro) pro[u].store(sm, (T_first + u) % R, tid);
-        } else {
-            for (int T = T_first; T <= c0 / kTile; ++T) {
-                st.load(kr, vr, rs, kTile * T - r0, tid);
-                st.store(sm, T % R, tid);
-            }
-            load_q(qa, c0);
-        }
-        for (int p0 = c0; p0 < c1; p0 += 2 * kTile) {
-            step(qa, qb, p0);
-            if (p0 + kTile >= c1) break;
-            step(qb, qa, p0 + kTile);
-        }
+        // The first step's Q and every window tile up to the step's own are
+        // all requested before any is waited for.
+        copy_q(c0);
+        for (int T = T_first; T <= c0 / kTile; ++T) copy_kv(T);   // <= ntw tiles
+        // The first step waits for all of them (no stores are in flight):
+        // vmcnt(NST) would leave some copies outstanding, so drain here.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        read_q(cur);
+        for (int p0 = c0; p0 < c1; p0 += kTile) step(p0);
     }
+    hold_until_done<0>(xo);                                       // nothing left in flight
 }
 
 }  // namespace
