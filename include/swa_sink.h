@@ -51,6 +51,7 @@
  *    rows of the same 32-key tile that do not (their weight for it is 0,
  *    and 0 * NaN = NaN in the matrix products); lse is unaffected.
  *  - Supported head dims: D in {64, 128}.
+ *  - A window larger than the sequence is the same as the whole sequence.
  *  - bfloat16 results are rounded to nearest-even from float32 accumulators.
  */
 #ifndef SWA_SINK_H
@@ -75,8 +76,10 @@ enum swa_status {
     SWA_OK = 0,
     SWA_ERR_NULL = -1,        /* a required pointer is NULL                        */
     SWA_ERR_SHAPE = -2,       /* negative size, Hq/Hkv/D/window < 1, Hq % Hkv != 0,
-                                 T_q > window, S_q > S_kv, B or Hq > 65535, or more
-                                 work units (B*Hq*rows/32, B*Hq*T_q) than 2^31-1  */
+                                 T_q > window, S_q > S_kv, B or Hq > 65535, a row
+                                 count (S, S_q, S_kv, T_q, max_seqlen, total) above
+                                 2^30, or more work units (B*Hq*rows/32, B*Hq*T_q)
+                                 than 2^31-1                                        */
     SWA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, unknown dtype, misaligned pointer,
                                  or window*D*2 > 2^31-1 bytes for one decode ring  */
     SWA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */

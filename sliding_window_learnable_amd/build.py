@@ -2,6 +2,11 @@
 
 Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
 parallel), then linked into ``sliding_window_learnable_amd/libswa_sink.so``.
+A second, debug-only library ``libswa_sink_poison.so`` is built the same
+way with ``-DSWA_LDS_POISON`` (objects in ``_build/poison/``): its kernels
+start from NaN-filled LDS and poison every copy's destination first, so a
+read of LDS that nothing has written yet shows up as NaN.  Only the tests
+load it; the package always loads ``libswa_sink.so``.
 Run as ``python -m sliding_window_learnable_amd.build``.
 """
 from __future__ import annotations
@@ -19,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libswa_sink.so")
+POISON_LIB_PATH = os.path.join(PKG, "libswa_sink_poison.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -54,29 +60,45 @@ def flags_for(src: str) -> list:
     return list(HIPCC_FLAGS)
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *flags_for(src), "-c", src, "-o", obj]
+def _compile(job) -> str:
+    src, out_dir, extra = job
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *flags_for(src), *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s" % (src, res.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libswa_sink.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(objs, path):
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s" % res.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Compile every HIP source and link libswa_sink.so (and, unless
+    poison=False, the LDS-poisoning debug library); returns the product
+    library's path."""
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    poison_dir = os.path.join(BUILD_DIR, "poison")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(src, BUILD_DIR, []) for src in sources]
+    if poison:
+        os.makedirs(poison_dir, exist_ok=True)
+        jobs += [(src, poison_dir, ["-DSWA_LDS_POISON"]) for src in sources]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(sources)], LIB_PATH)
     if verbose:
         print("built", LIB_PATH)
+    if poison:
+        _link(objs[len(sources):], POISON_LIB_PATH)
+        if verbose:
+            print("built", POISON_LIB_PATH)
     return LIB_PATH
 
 

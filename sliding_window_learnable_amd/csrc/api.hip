@@ -32,6 +32,15 @@ int status_of(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
 constexpr long kMaxGridX = 0x7fffffffL;
 bool grid_fits(long units) { return units >= 0 && units <= kMaxGridX; }
 
+// Row counts (sequence lengths, packed totals, query tokens) are at most
+// 2^30, so that position arithmetic in the kernels (a position plus a tile
+// or a window) stays inside 32-bit integers.
+constexpr int kMaxRows = 1 << 30;
+bool rows_ok(long n) { return n >= 0 && n <= kMaxRows; }
+
+// 32-row blocks of n rows, without overflow.
+long blocks32(int n) { return ((long)n + 31) / 32; }
+
 }  // namespace
 
 extern "C" {
@@ -40,14 +49,15 @@ int swa_sink_prefill(const void *q, const void *k, const void *v, const float *s
                      float *lse, int B, int Hq, int Hkv, int S, int D, int window, int dtype,
                      void *stream) {
     if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
-    if (S < 0 || window < 1) return SWA_ERR_SHAPE;
+    if (!rows_ok(S) || window < 1) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(sink, 4) || !aligned(lse, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S == 0) return SWA_OK;
-    if (!grid_fits((long)B * Hkv * ((S + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (!grid_fits((long)B * Hkv * blocks32(S) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (window > S) window = S;                       // every key of the sequence: same result
 
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S, S, D, window};
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -61,14 +71,15 @@ int swa_sink_prefill_varlen(const void *q, const void *k, const void *v, const f
                             int max_seqlen, int total, int Hq, int Hkv, int D, int window,
                             int dtype, void *stream) {
     if (!q || !k || !v || !sink || !out || !cu_seqlens) return SWA_ERR_NULL;
-    if (max_seqlen < 0 || total < 0 || window < 1) return SWA_ERR_SHAPE;
+    if (!rows_ok(max_seqlen) || !rows_ok(total) || window < 1) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(sink, 4) || !aligned(lse, 4) || !aligned(cu_seqlens, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || max_seqlen == 0 || total == 0) return SWA_OK;
-    if (!grid_fits((long)B * Hkv * ((max_seqlen + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (!grid_fits((long)B * Hkv * blocks32(max_seqlen) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (window > max_seqlen) window = max_seqlen;     // every key of each sequence
 
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, max_seqlen, max_seqlen, D,
                        window, cu_seqlens, total};
@@ -83,7 +94,7 @@ int swa_sink_decode(const void *q, const void *kcache, const void *vcache, const
                     void *out, float *lse, int B, int Hq, int Hkv, int T_q, int window, int D,
                     const int32_t *cache_len, int dtype, void *stream) {
     if (!q || !kcache || !vcache || !sink || !out) return SWA_ERR_NULL;
-    if (T_q < 0 || window < 1 || T_q > window) return SWA_ERR_SHAPE;
+    if (!rows_ok(T_q) || window < 1 || T_q > window) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(out, 16) ||
@@ -104,7 +115,7 @@ int swa_sink_decode_ring(const void *q, const void *kcache, const void *vcache, 
                          void *out, float *lse, int B, int Hq, int Hkv, int T_q, int window,
                          int ring, int D, const int32_t *cache_len, int dtype, void *stream) {
     if (!q || !kcache || !vcache || !sink || !out) return SWA_ERR_NULL;
-    if (T_q < 0 || window < 1 || ring < window || T_q > ring) return SWA_ERR_SHAPE;
+    if (!rows_ok(T_q) || window < 1 || ring < window || T_q > ring) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(out, 16) ||
@@ -126,7 +137,7 @@ int swa_sink_rope_append(const void *q, const void *k_new, const void *v_new, vo
                          int Hkv, int T_q, int ring, int D, double rope_theta, int dtype,
                          void *stream) {
     if (!q || !k_new || !v_new || !q_rot || !kcache || !vcache) return SWA_ERR_NULL;
-    if (T_q < 0 || ring < 1 || T_q > ring) return SWA_ERR_SHAPE;
+    if (!rows_ok(T_q) || ring < 1 || T_q > ring) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!(rope_theta > 1.0) || !std::isfinite(rope_theta)) return SWA_ERR_UNSUPPORTED;
@@ -142,7 +153,8 @@ int swa_sink_rope_append(const void *q, const void *k_new, const void *v_new, vo
 }
 
 size_t global_sink_attn_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_q < 1 || S_kv < S_q || !head_dim_ok(D))
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_q < 1 || S_kv < S_q ||
+        !rows_ok(S_kv) || !head_dim_ok(D))
         return 0;
     if (!swa::splitkv_preferred(Hq, Hkv, S_q, S_kv)) return 0;
     return swa::splitkv_workspace_bytes(B, Hq, Hkv, S_q, S_kv, D);
@@ -152,14 +164,14 @@ int global_sink_attn(const void *q, const void *k, const void *v, const float *s
                      float *lse, int B, int Hq, int Hkv, int S_q, int S_kv, int D,
                      void *workspace, size_t workspace_bytes, int dtype, void *stream) {
     if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
-    if (S_q < 0 || S_kv < 0 || S_q > S_kv) return SWA_ERR_SHAPE;
+    if (!rows_ok(S_q) || !rows_ok(S_kv) || S_q > S_kv) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(sink, 4) || !aligned(lse, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S_q == 0) return SWA_OK;
-    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (!grid_fits((long)B * Hkv * blocks32(S_q) * (Hq / Hkv))) return SWA_ERR_SHAPE;
 
     // Every key position is inside the window: window = S_kv.
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
@@ -178,14 +190,14 @@ int global_sink_attn_noalloc(const void *q, const void *k, const void *v, const 
                              void *out, float *lse, int B, int Hq, int Hkv, int S_q, int S_kv,
                              int D, int dtype, void *stream) {
     if (!q || !k || !v || !sink || !out) return SWA_ERR_NULL;
-    if (S_q < 0 || S_kv < 0 || S_q > S_kv) return SWA_ERR_SHAPE;
+    if (!rows_ok(S_q) || !rows_ok(S_kv) || S_q > S_kv) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(sink, 4) || !aligned(lse, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S_q == 0) return SWA_OK;
-    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (!grid_fits((long)B * Hkv * blocks32(S_q) * (Hq / Hkv))) return SWA_ERR_SHAPE;
 
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -203,7 +215,7 @@ int global_sink_attn_block_max(const void *q, const void *k, const void *v, cons
                                int Hq, int Hkv, int S_q, int S_kv, int D, int dtype,
                                void *stream) {
     if (!q || !k || !v || !sink || !out || !block_max) return SWA_ERR_NULL;
-    if (S_q < 0 || S_kv < 0 || S_q > S_kv || block_k < 32 || block_k % 32 != 0)
+    if (!rows_ok(S_q) || !rows_ok(S_kv) || S_q > S_kv || block_k < 32 || block_k % 32 != 0)
         return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
@@ -212,7 +224,7 @@ int global_sink_attn_block_max(const void *q, const void *k, const void *v, cons
         !aligned(sink, 4) || !aligned(lse, 4) || !aligned(block_max, 4))
         return SWA_ERR_UNSUPPORTED;
     if (B == 0 || S_q == 0) return SWA_OK;
-    if (!grid_fits((long)B * Hkv * ((S_q + 31) / 32) * (Hq / Hkv))) return SWA_ERR_SHAPE;
+    if (!grid_fits((long)B * Hkv * blocks32(S_q) * (Hq / Hkv))) return SWA_ERR_SHAPE;
 
     swa::PrefillArgs a{q, k, v, sink, out, lse, B, Hq, Hkv, S_q, S_kv, D, S_kv};
     return status_of(
@@ -220,7 +232,7 @@ int global_sink_attn_block_max(const void *q, const void *k, const void *v, cons
 }
 
 size_t swa_sink_backward_workspace_bytes(int B, int Hq, int S) {
-    if (B < 1 || Hq < 1 || S < 1) return 0;
+    if (B < 1 || Hq < 1 || S < 1 || !rows_ok(S)) return 0;
     return swa::backward_workspace_bytes(B, Hq, S);
 }
 
@@ -230,7 +242,7 @@ int swa_sink_backward(const void *q, const void *k, const void *v, const float *
                       void *workspace, size_t workspace_bytes, int dtype, void *stream) {
     if (!q || !k || !v || !sink || !out || !lse || !dout || !dq || !dk || !dv || !dsink)
         return SWA_ERR_NULL;
-    if (S < 0 || window < 1) return SWA_ERR_SHAPE;
+    if (!rows_ok(S) || window < 1) return SWA_ERR_SHAPE;
     const int rc = common_checks(B, Hq, Hkv, D, dtype);
     if (rc != SWA_OK) return rc;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -257,8 +269,9 @@ const char *swa_sink_strerror(int code) {
     case SWA_OK: return "success";
     case SWA_ERR_NULL: return "a required pointer argument is NULL";
     case SWA_ERR_SHAPE:
-        return "invalid sizes (negative size, Hq % Hkv != 0, window < 1, T_q > window, "
-               "S_q > S_kv, batch/heads above 65535, or more work units than one launch holds)";
+        return "invalid sizes (negative size, more than 2^30 rows, Hq % Hkv != 0, window < 1, "
+               "T_q > window, S_q > S_kv, batch/heads above 65535, or more work units than one "
+               "launch holds)";
     case SWA_ERR_UNSUPPORTED:
         return "unsupported argument (head dim not 64/128, unknown dtype, a pointer not "
                "aligned to 16 bytes, or a ring cache above 2 GiB per (sequence, KV head))";

@@ -207,6 +207,52 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// LDS poisoning, for debug builds (-DSWA_LDS_POISON; never in the product
+// library).  Every kernel fills its LDS with NaN patterns on entry, and every
+// buffer->LDS copy first overwrites the 16 bytes per lane it is about to
+// fill: a read of LDS that no copy or store has reached yet -- a slot read
+// before its copy landed (a missing wait or barrier), a tile never staged,
+// a stale slot index -- then yields NaN in the results instead of plausible
+// old values.  Results of a correct kernel are bit-identical either way.
+// ---------------------------------------------------------------------------
+#ifdef SWA_LDS_POISON
+constexpr bool kLdsPoison = true;
+#else
+constexpr bool kLdsPoison = false;
+#endif
+constexpr uint32_t kPoisonWord = 0x7FC17FC1u;   // two bf16 NaNs, also an fp32 NaN
+
+// Whole-work-group fill of an LDS object, then a barrier.  Every wave of the
+// work-group must call it (before any early return).
+template <class T>
+__device__ __forceinline__ void lds_poison_all(T &obj) {
+    if constexpr (kLdsPoison) {
+        uint32_t *w = reinterpret_cast<uint32_t *>(&obj);
+        for (unsigned i = threadIdx.x; i < sizeof(T) / 4; i += blockDim.x) w[i] = kPoisonWord;
+        __syncthreads();
+    }
+}
+// One wave's fill of its own LDS object (no barrier: only this wave uses it).
+template <class T>
+__device__ __forceinline__ void lds_poison_wave(T &obj) {
+    if constexpr (kLdsPoison) {
+        uint32_t *w = reinterpret_cast<uint32_t *>(&obj);
+        for (unsigned i = threadIdx.x & 63; i < sizeof(T) / 4; i += 64) w[i] = kPoisonWord;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+// The 16 bytes a copy of this lane will write at lds + 16 * lane.
+__device__ __forceinline__ void lds_poison_lane16(const void *lds) {
+    if constexpr (kLdsPoison) {
+        const unsigned la =
+            (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds + 16u * (threadIdx.x & 63);
+        u32x4 p;
+        p[0] = p[1] = p[2] = p[3] = kPoisonWord;
+        asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(la), "v"(p) : "memory");
+    }
+}
+
 // Buffer -> LDS copy (no registers): lane l's 16 bytes at voff land at
 // lds + 16 l; out-of-range dwords land as zero.  Written as asm so that the
 // compiler does not wait for every copy before each LDS read (it cannot
@@ -216,6 +262,7 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
+    lds_poison_lane16(lds);
     const unsigned la = __builtin_amdgcn_readfirstlane(
         (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(la),
@@ -225,6 +272,7 @@ __device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
 // The same copy with the non-temporal cache policy, for data read exactly
 // once in whole cache lines per instruction.
 __device__ __forceinline__ void dma16_nt(u32x4 r, const void *lds, uint32_t voff) {
+    lds_poison_lane16(lds);
     const unsigned la = __builtin_amdgcn_readfirstlane(
         (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(la),

@@ -21,7 +21,7 @@
 namespace swa {
 namespace {
 
-constexpr int kRows = 32;     // rows per pre-pass work unit
+constexpr int kRows = kBackwardRows;     // rows per pre-pass work unit
 
 // Dot product of one 16-byte piece of two rows (8 bf16 or 4 float elements).
 __device__ __forceinline__ float dot16(const bf16 *x, const bf16 *y) {
@@ -198,11 +198,6 @@ template <class T>
 hipError_t launch_generic(const BackwardArgs &a, hipStream_t stream);
 
 }  // namespace
-
-size_t backward_workspace_bytes(int B, int Hq, int S) {
-    const size_t tiles = (size_t)(S + kRows - 1) / kRows;
-    return 4 * (size_t)B * Hq * (2 * (size_t)S + tiles);
-}
 
 namespace {
 

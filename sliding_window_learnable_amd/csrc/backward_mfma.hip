@@ -57,6 +57,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const float *__restrict__ sink, float *__restrict__ dsum, float *__restrict__ l2g,
     float *__restrict__ part, bf16 *__restrict__ dq, int S, int Hq, int Hkv, int W, int BG, int NB) {
     __shared__ __align__(16) DqSmem<D> sm;
+    lds_poison_all(sm);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
     const bf16 *__restrict__ dout, const float *__restrict__ l2g, const float *__restrict__ dsum,
     bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int Hq, int Hkv, int W, int BG) {
     __shared__ __align__(16) KvSmem<D, NW> sm;
+    lds_poison_all(sm);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

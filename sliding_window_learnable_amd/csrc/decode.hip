@@ -67,6 +67,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     const int G = Hq / Hkv;
     bf16 (*kt)[D + kKtPad] = kt_all[wave];
     bf16 (*vt)[kChunk + kVtPad] = vt_all[wave];
+    lds_poison_wave(kt_all[wave]);
+    lds_poison_wave(vt_all[wave]);
     const float c = kLog2e / sqrtf((float)D);
 
     // This lane's column: token t, query head h.
@@ -353,30 +355,6 @@ hipError_t ring_decode_d(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Enough waves to give every SIMD two: each wave streams one key range.
-constexpr int kSplitTargetWaves = 2048;
-
-struct SplitPlan {
-    int n_splits, kps, n_ct;
-};
-
-SplitPlan plan_split(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {
-    const int G = Hq / Hkv;
-    const int n_ct = (G * S_q + 31) / 32;
-    const int ck = kChunk;
-    const long pairs = (long)B * Hkv * n_ct;
-    const int max_splits = (S_kv + ck - 1) / ck;
-    int want = (int)((kSplitTargetWaves + pairs - 1) / pairs);
-    want = max(1, min(want, max_splits));
-    int kps = (S_kv + want - 1) / want;
-    kps = ((kps + ck - 1) / ck) * ck;
-    // Each split's buffer window (kps rows of all KV heads) stays below 2^31 bytes.
-    const long cap = ((1L << 31) / ((long)Hkv * D * 2)) / ck * ck;
-    if (kps > cap) kps = (int)cap;
-    const int n_splits = (S_kv + kps - 1) / kps;
-    return {n_splits, kps, n_ct};
-}
-
 template <int D>
 hipError_t splitkv_d(const PrefillArgs &a, void *workspace, hipStream_t stream) {
     const SplitPlan p = plan_split(a.B, a.Hq, a.Hkv, a.S, a.S_kv, a.D);
@@ -398,20 +376,6 @@ hipError_t splitkv_d(const PrefillArgs &a, void *workspace, hipStream_t stream) 
 
 hipError_t launch_ring_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
     return a.D == 64 ? ring_decode_d<64>(a, stream) : ring_decode_d<128>(a, stream);
-}
-
-int splitkv_num_splits(int B, int Hq, int Hkv, int S_q, int S_kv) {
-    return plan_split(B, Hq, Hkv, S_q, S_kv, 128).n_splits;
-}
-
-bool splitkv_preferred(int Hq, int Hkv, int S_q, int S_kv) {
-    (void)S_kv;
-    return (long)(Hq / Hkv) * S_q <= 64;
-}
-
-size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D) {
-    const SplitPlan p = plan_split(B, Hq, Hkv, S_q, S_kv, D);
-    return (size_t)p.n_splits * B * Hq * S_q * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_splitkv_bf16(const PrefillArgs &a, void *workspace, hipStream_t stream) {

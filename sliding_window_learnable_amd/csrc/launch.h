@@ -61,6 +61,12 @@ hipError_t launch_stream_bf16_block_max(const PrefillArgs &a, float *bmax, int b
 hipError_t launch_ring_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 
 // bf16 split-KV partials over a linear cache + combine (sink added once).
+struct SplitPlan {
+    int n_splits;               // key ranges per (sequence, KV head, column tile)
+    int kps;                    // keys per range (a multiple of 32)
+    int n_ct;                   // 32-column tiles of (token, head) pairs
+};
+SplitPlan plan_split(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
 int splitkv_num_splits(int B, int Hq, int Hkv, int S_q, int S_kv);
 bool splitkv_preferred(int Hq, int Hkv, int S_q, int S_kv);
 size_t splitkv_workspace_bytes(int B, int Hq, int Hkv, int S_q, int S_kv, int D);
@@ -84,6 +90,7 @@ struct BackwardArgs {
     float *ws_part;             // [B, Hq, ceil(S/32)]: sink-gradient partials
     int B, Hq, Hkv, S, D, window;
 };
+constexpr int kBackwardRows = 32;      // rows per sink-gradient partial
 size_t backward_workspace_bytes(int B, int Hq, int S);
 hipError_t launch_backward_pre(const BackwardArgs &a, hipStream_t stream, bool bf16_inputs);
 // dsink_h = -(sum of the per-32-row partials in ws_part), fixed order.

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     }
     const int i0 = qb * kTile;                         // first query row of the block
     if (i0 >= S_q) return;                             // past this sequence (uniform, before any barrier)
+    lds_poison_all(sm);
     const int off = S_kv - S_q;                        // row i sits at position off + i
     const int p_first = off + i0;
     const int p_last = off + min(S_q - 1, i0 + kTile - 1);

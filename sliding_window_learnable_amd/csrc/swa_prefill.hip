@@ -88,6 +88,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     constexpr int NST = 2 * (D / 32) + 1;                        // stores per step (out, lse)
     static_assert(IPW >= 1 && IPW * NW == NI, "copy split");
     __shared__ __align__(16) RingSmem<D, NW> sm;
+    lds_poison_all(sm);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -449,17 +450,6 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 
 }  // namespace
 
-// Largest chunk (a multiple of 32 positions) whose buffer windows stay below
-// 2^31 bytes: q/out rows [c0, c1) of all heads, k/v rows [r0, c1) of one KV
-// head including the (ntw-1)-tile halo.
-int prefill_chunk_cap(int Hq, int Hkv, int D, int ntw) {
-    const long limit = 1L << 31;
-    const long q_rows = limit / ((long)Hq * D * 2);
-    const long kv_rows = limit / ((long)Hkv * D * 2) - (long)kTile * (ntw - 1);
-    const long rows = q_rows < kv_rows ? q_rows : kv_rows;
-    return (int)(rows < kTile ? kTile : (rows / kTile) * kTile);
-}
-
 namespace {
 
 template <int D, int NW>
@@ -511,11 +501,6 @@ hipError_t launch_ring_d(const PrefillArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
-
-bool prefill_ring_supported(int window, int G) {
-    const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
-    return window >= 98 && window <= 129 && g_ok;         // exactly five 32-key tiles
-}
 
 hipError_t launch_prefill_ring_bf16(const PrefillArgs &a, hipStream_t stream) {
     return a.D == 64 ? launch_ring_d<64>(a, stream) : launch_ring_d<128>(a, stream);

@@ -56,6 +56,7 @@ def pytest_terminal_summary(terminalreporter):
     for what, dt, rel, bar, plain, abs_err, _rms in GRAD_REPORT:
         w = worst.setdefault((what, dt), [0.0, bar, 0.0, 0.0, 0])
         w[0], w[2], w[3] = max(w[0], rel), max(w[2], plain), max(w[3], abs_err)
+        w[1] = max(w[1], bar)             # the loosest bar applied (per-case bars)
         w[4] += 1
     tr.write_line("%-6s %-9s %7s %14s %6s %19s %10s" % (
         "grad", "dtype", "checks", "err/(rms+|r|)", "bar", "err/(2e-2+1e-2|r|)", "max |err|"))
