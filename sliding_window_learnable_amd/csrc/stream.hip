@@ -21,12 +21,21 @@
 // iteration t a wave issues the S^T products of tile t+1 before the
 // softmax of tile t (so the matrix unit and the vector unit work at once),
 // then the PV products of tile t; the copies of tile t+3 go to the slot
-// tile t-1 freed.  One barrier per tile.  Work-groups are issued longest-first
-// (the last query blocks have the most keys) with the (batch, KV head)
-// index fastest, so the blocks of one KV head share an XCD and its L2.
-// Packed batches of sequences of different lengths give each work-group its
-// sequence's first row and length from the row-offset table; blocks past a
-// sequence's end return before touching memory or a barrier.
+// tile t-1 freed.  One barrier per tile.
+//
+// Work order: the KV head index is the fastest (consecutive work-groups go
+// to different XCDs, so the blocks of one KV head share an XCD and its
+// L2), then the query blocks of one sequence, longest first (the last
+// query blocks have the most keys), then the sequences.  So the
+// work-groups that run together on an XCD mostly belong to one sequence
+// and read the same key tiles through its L2; taken in query-block order
+// across the batch, the 32 or so resident work-groups of an XCD would
+// belong to as many sequences as the batch holds and share almost nothing.
+// Packed batches of sequences of different lengths: sequence s owns the
+// 32-row slots j with 32j in [cu[s] + 32s, cu[s+1] + 32(s+1)), at least
+// ceil(len_s / 32) of them, with no table built on the host; a work-group
+// finds its sequence by a 64-way search of cu and returns before touching
+// memory or a barrier when its slot is a spare one.
 #include "attn_device.h"
 #include "launch.h"
 
@@ -62,22 +71,47 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lq = lane & 31, hl = lane >> 5;
-    const int bg = blockIdx.x % BG;
-    const int qb = NB - 1 - blockIdx.x / BG;          // longest query blocks first
-    const int b = bg / Hkv, g = bg % Hkv;
     const int G = Hq / Hkv;
     const float c = kLog2e / sqrtf((float)D);
 
     // Packed variable-length batch (cu != nullptr): sequence b owns rows
     // cu[b] .. cu[b+1]-1 of [total, H, D] tensors (lse [Hq, total]) and
     // attends within itself; otherwise [B, S, H, D] (lse [B, Hq, S_q]).
-    int S_q = S_q_, S_kv = S_kv_;
-    size_t q_row0 = (size_t)b * S_q_, kv_row0 = (size_t)b * S_kv_;
-    if (cu != nullptr) {   // clamped so a malformed table cannot index past the tensors
+    int S_q = S_q_, S_kv = S_kv_, b, g, qb;
+    size_t q_row0, kv_row0;
+    if (cu == nullptr) {
+        g = blockIdx.x % Hkv;
+        const int j = blockIdx.x / Hkv;
+        b = j / NB;
+        qb = NB - 1 - j % NB;                          // longest query blocks first
+        q_row0 = (size_t)b * S_q_;
+        kv_row0 = (size_t)b * S_kv_;
+    } else {
+        // Table values are clamped to [0, total] throughout, so a malformed
+        // table cannot index past the tensors (nor stop the search).
+        const int B = BG / Hkv;                        // sequences
+        g = blockIdx.x % Hkv;
+        const long slot = (long)(blockIdx.x / Hkv) * kTile;
+        auto start = [&](int s) {                      // 32s + cu[s], clamped
+            return (long)kTile * s + min(max(cu[s], 0), total);
+        };
+        if (start(0) > slot) return;
+        int lo = 0, hi = B;                            // start(lo) <= slot
+        while (hi - lo > 1) {                          // wave-uniform
+            const int step = (hi - lo + 63) / 64, s = lo + lane * step;
+            const uint64_t ok = __ballot(s < hi && start(min(s, B)) <= slot);
+            const int last = 63 - __builtin_clzll(ok);  // lane 0 (s = lo) always passes
+            lo += last * step;
+            hi = min(hi, lo + step);
+        }
+        b = lo;
         const int s0 = min(max(cu[b], 0), total);
         const int s1 = min(max(cu[b + 1], s0), min(total, s0 + S_q_));
         S_q = S_kv = s1 - s0;
         q_row0 = kv_row0 = (size_t)s0;
+        const long first = (start(b) + kTile - 1) / kTile;   // the sequence's first slot
+        qb = (S_q + kTile - 1) / kTile - 1 - (int)(slot / kTile - first);   // longest first
+        if (qb < 0) return;                            // a spare slot (uniform, before any barrier)
     }
     const int i0 = qb * kTile;                         // first query row of the block
     if (i0 >= S_q) return;                             // past this sequence (uniform, before any barrier)
@@ -335,7 +369,11 @@ template <int D, int NW, bool BLK>
 hipError_t launch(const PrefillArgs &a, float *bmax, int block_k, hipStream_t stream) {
     const int BG = a.B * a.Hkv;
     const int NB = (a.S + kTile - 1) / kTile;
-    const long n_wg = (long)BG * NB;
+    // Packed: one slot per 32 rows plus one per sequence, for each KV head.
+    const long n_wg = a.cu_seqlens != nullptr
+                          ? (long)a.Hkv * (((long)a.total + kTile - 1) / kTile + a.B)
+                          : (long)BG * NB;
+    if (n_wg * NW * 64 > (long)UINT32_MAX) return hipErrorInvalidConfiguration;
     const int rk = block_k / kTile, NKB = (a.S_kv + block_k - 1) / block_k;
     hipLaunchKernelGGL((stream_attn_kernel<D, NW, BLK>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
                        stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.sink,
