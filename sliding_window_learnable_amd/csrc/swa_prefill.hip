@@ -336,7 +336,13 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         // out = O / l in bf16 (RNE): each lane writes its two 8-dim chunks
         // per 32-dim tile into the staging tile (row = its query), then
         // every lane reads back one 16-byte chunk of whole rows and stores
-        // it; rows past the window are dropped by the buffer range.
+        // it; rows past the window are dropped by the buffer range.  The
+        // staging rows rotate their chunks by row (chunk c of row r at
+        // c ^ (r % CPR)), not by the operand swizzle: 16-byte LDS writes
+        // are served 8 lanes at a time by 32 banks, so the 8 rows of a lane
+        // group must land on 8 different chunks modulo 8 (the operand
+        // swizzle, built for reads, pairs rows r and r + 2 there and
+        // doubled the writes' LDS time).
         const uint32_t so = (uint32_t)(p0 - c0) * qrow_bytes;
         bf16(*stg)[D] = sm.q[wave];
         {
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w[2 * dt + e][i] = (bf16)(o[dt][8 * e + i] * inv);
                     const int ch = (32 * dt + 16 * e + 8 * hl) / 8;
-                    *(bf16x8 *)&stg[lq][8 * (ch ^ qrow_s)] = w[2 * dt + e];
+                    *(bf16x8 *)&stg[lq][8 * (ch ^ (lq % CPR))] = w[2 * dt + e];
                 }
             lds_settle(w);
         }
@@ -357,7 +363,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 #pragma unroll
         for (int u = 0; u < QI; ++u) {
             const int row = RPI * u + lane / CPR;
-            buf_store16_nt(xo[u], orr, row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row)), so);
+            buf_store16_nt(xo[u], orr, row * qrow_bytes + 16 * ((lane % CPR) ^ (row % CPR)), so);
         }
         buf_store_f32(l == 0.0f ? -INFINITY : (mu + __builtin_amdgcn_logf(l)) * kLn2, lr, l_lane,
                       (uint32_t)(p0 - c0) * 4);
