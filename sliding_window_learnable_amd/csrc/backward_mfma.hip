@@ -9,8 +9,10 @@
 // in the permuted order of score_row_key so that accumulator registers
 // 8kk..8kk+7 are the B operand of the next product's kk-th K=16 step).
 //
-// dq: one work-group per (batch, KV head, 32 query rows), one wave per query
-//   head of the group; key tiles stream through LDS (K rows, V rows, K^T).
+// dq: one work-group per (batch, KV head, 32 query rows, set of at most four
+//   query heads of the group), one wave per query head; key tiles stream
+//   through LDS (K rows, V rows, K^T).  Four-wave work-groups let two of them
+//   share a CU, so one loads its rows while the other computes.
 //   Per tile: S^T = K Q^T, dP^T = V dO^T (lane = query), P^T, dS^T, and
 //   dQ^T += K^T dS^T.
 // dk/dv: one work-group per (batch, KV head, NW consecutive 32-key tiles),
@@ -46,8 +48,10 @@ struct DqSmem {
     bf16 v[kDqSlots][kTile][D];     // V rows (swizzled): A of dP^T = V dO^T
 };
 
-// One work-group per (batch, KV head, 32 query rows), one wave per query
-// head (NW at a time).  Before the key loop a wave also computes, for its
+// One work-group per (batch, KV head, 32 query rows, head set), one wave per
+// query head: head set hs holds heads hs*NW .. hs*NW+NW-1 of the group (HS
+// sets).  Work-groups run KV head fastest (one XCD per KV head), then head
+// set, then query block (longest first), then sequence.  Before the key loop a wave also computes, for its
 // rows, D_i = dO_i . O_i and lse_i log2(e) (written to the workspace for
 // the dk/dv kernel) and the row tile's sink-gradient partial.
 template <int D, int NW>
@@ -55,16 +59,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ out, const bf16 *__restrict__ dout, const float *__restrict__ lse,
     const float *__restrict__ sink, float *__restrict__ dsum, float *__restrict__ l2g,
-    float *__restrict__ part, bf16 *__restrict__ dq, int S, int Hq, int Hkv, int W, int BG, int NB) {
+    float *__restrict__ part, bf16 *__restrict__ dq, int S, int Hq, int Hkv, int W, int BG, int NB,
+    int HS) {
     __shared__ __align__(16) DqSmem<D> sm;
     lds_poison_all(sm);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 31, hl = lane >> 5;
-    const int bg = blockIdx.x % BG;
-    const int qb = NB - 1 - blockIdx.x / BG;              // longest query blocks first
-    const int b = bg / Hkv, g = bg % Hkv;
+    const int g = blockIdx.x % Hkv;
+    const int rest = blockIdx.x / Hkv;
+    const int hs = rest % HS;
+    const int qb = NB - 1 - (rest / HS) % NB;             // longest query blocks first
+    const int b = rest / HS / NB;
     const int G = Hq / Hkv;
     const float c = kLog2e / sqrtf((float)D);
     const float scale = 1.0f / sqrtf((float)D);
@@ -121,9 +128,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
     const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
 
-    for (int hh = wave; hh < G; hh += NW) {
+    for (int hh = hs * NW + wave; hh < G; hh += NW * HS) {
         const int h = g * G + hh;
-        if (hh != wave) lds_barrier();                     // previous head's tiles released
+        if (hh != hs * NW + wave) lds_barrier();           // previous head's tiles released
 
         // K/V tiles 0..2 start copying before the row loads, so the two
         // latencies overlap.
@@ -525,10 +532,11 @@ template <int D, int NW>
 hipError_t launch_dq(const BackwardArgs &a, hipStream_t stream) {
     const int BG = a.B * a.Hkv;
     const int NB = (a.S + kTile - 1) / kTile;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)((long)BG * NB)), dim3(NW * 64), 0,
+    const int HS = (a.Hq / a.Hkv) / NW;                    // head sets per group
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)((long)BG * NB * HS)), dim3(NW * 64), 0,
                        stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                        (const bf16 *)a.out, (const bf16 *)a.dout, a.lse, a.sink, a.ws_dsum, a.ws_l2,
-                       a.ws_part, (bf16 *)a.dq, a.S, a.Hq, a.Hkv, a.window, BG, NB);
+                       a.ws_part, (bf16 *)a.dq, a.S, a.Hq, a.Hkv, a.window, BG, NB, HS);
     return hipGetLastError();
 }
 
@@ -550,7 +558,7 @@ template <int D>
 hipError_t launch_d(const BackwardArgs &a, hipStream_t stream) {
     hipError_t e;
     switch (waves_for_group(a.Hq / a.Hkv)) {
-    case 8: e = launch_dq<D, 8>(a, stream); break;
+    case 8:
     case 4: e = launch_dq<D, 4>(a, stream); break;
     case 2: e = launch_dq<D, 2>(a, stream); break;
     default: e = launch_dq<D, 1>(a, stream); break;
