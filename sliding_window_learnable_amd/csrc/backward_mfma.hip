@@ -259,13 +259,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 
 constexpr int kKvSlots = 4;     // staging slots: pairs n, n+1 in use, n+2 landed, n+3 in flight
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int NW>
 struct KvSmem {
     bf16 q[kKvSlots][kTile][D];     // Q rows (swizzled): A of S = Q K^T, read transposed for dK
     bf16 g[kKvSlots][kTile][D];     // dO rows (swizzled): A of dP = dO V^T, transposed for dV
     float l2[kKvSlots][kTile];      // lse * log2(e) (0 past the end, where dO = 0)
     float dd[kKvSlots][kTile];      // D_i
-    f32x4 px[2][NW][4][64];         // P of each key tile, from its S wave to its dP wave
+    f16x4 px[2][NW][4][64];         // P of each key tile (fp16), from its S wave to its dP wave
 };
 
 template <int V>
@@ -275,7 +277,8 @@ struct IntC {
 
 // NW key tiles per work-group, two waves per tile: waves 0..NW-1 compute
 // S = Q K^T, P and dV^T += dO^T P (K in registers); waves NW..2NW-1 compute
-// dP = dO V^T, dS = P (dP - D) with P handed over through LDS, and
+// dP = dO V^T, dS = P (dP - D) with P handed over through LDS in fp16 (so
+// that a two-tile work-group fits twice in a CU's LDS), and
 // dK^T += Q^T dS (V in registers).  The S waves run one pair ahead: in
 // step n they compute P of pair n+1 and dV of pair n while the dP waves
 // finish pair n, so each step has one barrier.  Q, lse (S waves) and dO, D
@@ -345,12 +348,12 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
         const int r0 = qt * kTile;
         // rows i = r0 + perm_row(r, hl), key j = j0 + lq: visible iff j <= i < j + W
         const bool masked = qt == kt || (qt * kTile + kTile - 1) - W >= j0;
-        f32x4 *px = sm.px[pbuf][slot][0] + lane;
+        f16x4 *px = sm.px[pbuf][slot][0] + lane;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
             const f32x4 l2v = *(const f32x4 *)&sm.l2[bi][row];
-            f32x4 pv;
+            f16x4 pv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * u + e;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
                     y = (dij >= 0 && dij < W) ? y : -INFINITY;
                 }
                 x[r] = __builtin_amdgcn_exp2f(fmaf(y, c, -l2v[e]));
-                pv[e] = x[r];
+                pv[e] = (_Float16)x[r];
             }
             px[64 * u] = pv;
         }
@@ -478,12 +481,12 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
             if (copy) stage((n + 3) % kKvSlots);
             if (active(qt)) {
                 f32x16 x = scores(bi);
-                const f32x4 *px = sm.px[n & 1][slot][0] + lane;
+                const f16x4 *px = sm.px[n & 1][slot][0] + lane;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
                     const f32x4 ddv = *(const f32x4 *)&sm.dd[bi][row];
-                    const f32x4 pv = px[64 * u];
+                    const f16x4 pv = px[64 * u];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[4 * u + e] = pv[e] * (x[4 * u + e] - ddv[e]);
                 }
@@ -540,18 +543,28 @@ hipError_t launch_dq(const BackwardArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-constexpr int kKvWaves = 4;        // key tiles per dk/dv work-group (two waves each)
+// Key tiles per dk/dv work-group (two waves each).  A work-group walks the
+// query tiles that see any of its keys, so narrow windows read each Q/dO
+// tile (NW + nvis - 1) / NW times, nvis being the query tiles one key tile
+// sees; two key tiles read more of them than four, but two such work-groups
+// share a CU and hide each other's copy latency.  Measured at S = 32768:
+// two tiles win up to window 256 (1.124 vs 1.201 ms at 128), tie at 512,
+// and lose from 1024 on (5.01 vs 4.77 ms) and for the global layer.
+template <int D, int NW>
+hipError_t launch_dkdv_nw(const BackwardArgs &a, hipStream_t stream) {
+    const int BG = a.B * a.Hkv;
+    const int nKT = (a.S + kTile - 1) / kTile;
+    const int nblk = (nKT + NW - 1) / NW;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3((unsigned)((long)BG * nblk)), dim3(2 * NW * 64),
+                       0, stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                       (const bf16 *)a.dout, a.ws_l2, a.ws_dsum, (bf16 *)a.dk, (bf16 *)a.dv, a.S,
+                       a.Hq, a.Hkv, a.window, BG);
+    return hipGetLastError();
+}
 
 template <int D>
 hipError_t launch_dkdv(const BackwardArgs &a, hipStream_t stream) {
-    const int BG = a.B * a.Hkv;
-    const int nKT = (a.S + kTile - 1) / kTile;
-    const int nblk = (nKT + kKvWaves - 1) / kKvWaves;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kKvWaves>), dim3((unsigned)((long)BG * nblk)),
-                       dim3(2 * kKvWaves * 64), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                       (const bf16 *)a.v, (const bf16 *)a.dout, a.ws_l2, a.ws_dsum, (bf16 *)a.dk,
-                       (bf16 *)a.dv, a.S, a.Hq, a.Hkv, a.window, BG);
-    return hipGetLastError();
+    return a.window <= 256 ? launch_dkdv_nw<D, 2>(a, stream) : launch_dkdv_nw<D, 4>(a, stream);
 }
 
 template <int D>

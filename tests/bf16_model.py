@@ -2,8 +2,9 @@
 
 The bf16 backward kernels round at fixed points: the forward's output O
 (bf16, so D_i = dO_i . O_i uses the rounded O), the probabilities P fed to
-the dV product, the score gradients dS fed to the dQ and dK products, and
-the gradients themselves.  ``rounded_backward`` evaluates the backward in
+the dV product, P again where the dk/dv kernel hands it from the wave that
+computes it to the wave that forms dS for dK (fp16), the score gradients dS
+fed to the dQ and dK products, and the gradients themselves.  ``rounded_backward`` evaluates the backward in
 fp64 with exactly those rounding points and no other error, so its distance
 from the exact oracle is the floor any correct kernel with these rounding
 points reaches on the same inputs.  It is dense (masked S x S matrices), for
@@ -22,11 +23,19 @@ def rb(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x)).to(BF16).double().numpy()
 
 
-def rounded_backward(q, k, v, sink, dout, W, rnd=rb, rnd_out=None):
+def rh(x: np.ndarray) -> np.ndarray:
+    """Round to fp16 (nearest-even) and back to fp64."""
+    return np.ascontiguousarray(x).astype(np.float16).astype(np.float64)
+
+
+def rounded_backward(q, k, v, sink, dout, W, rnd=rb, rnd_out=None, rnd_pk=None):
     """fp64 backward with the bf16 kernels' rounding points (see the module
     notes); ``rnd`` is the rounding applied at each of them, ``rnd_out`` (if
-    given) the one applied to the forward's O instead."""
+    given) the one applied to the forward's O instead, ``rnd_pk`` the one of
+    the P that forms dS for dK (default: fp16 when ``rnd`` is bf16, else
+    ``rnd``)."""
     r_o = rnd if rnd_out is None else rnd_out
+    r_pk = (rh if rnd is rb else rnd) if rnd_pk is None else rnd_pk
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -55,8 +64,9 @@ def rounded_backward(q, k, v, sink, dout, W, rnd=rb, rnd_out=None):
             dv[b, :, g] += Pb.T @ dout[b, :, h]
             dP = dout[b, :, h] @ v[b, :, g].T
             dS = rnd(P * (dP - Di[:, None]))
+            dSk = rnd(r_pk(P) * (dP - Di[:, None]))
             dq[b, :, h] = scale * (dS @ k[b, :, g])
-            dk[b, :, g] += scale * (dS.T @ q[b, :, h])
+            dk[b, :, g] += scale * (dSk.T @ q[b, :, h])
             if not np.isneginf(s):
                 dsink[h] -= (np.exp(s - lse) * Di).sum()
     return rnd(dq), rnd(dk), rnd(dv), dsink

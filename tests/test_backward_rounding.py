@@ -2,8 +2,8 @@
 
 The bf16 backward rounds at fixed points: the forward's output O (bf16, so
 D_i = dO_i . O_i uses the rounded O), the probabilities P fed to the dV
-product, the score gradients dS fed to the dQ and dK products, and the
-gradients themselves.  This test evaluates the backward in fp64 with exactly
+product, P as handed (in fp16) to the wave that forms dS for dK, the score
+gradients dS fed to the dQ and dK products, and the gradients themselves.  This test evaluates the backward in fp64 with exactly
 those rounding points and no other error (numpy/torch, dense masked
 matrices), and measures how far that moves the result from the exact fp64
 oracle, in the unit the GPU tests use: |err| / (rms(ref) + |ref|).
