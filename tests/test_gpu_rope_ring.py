@@ -25,6 +25,9 @@ def gen(seed, shape, dtype, scale=1.0):
     (3, 4, 8, 1, 131, 128, [0, 200, 1_000_003]),
     (2, 1, 16, 2, 128, 64, [5, 127]),
     (2, 3, 6, 2, 100, 128, [262_141, 99]),
+    # malformed (negative) cache lengths: slots are P mod ring in [0, ring),
+    # so every write stays inside its own sequence's ring
+    (3, 4, 8, 1, 131, 128, [-1, -5, -136]),
 ])
 def test_rope_append_matches_oracle(gpu, dtype, B, T, Hq, Hkv, R, D, lens):
     q = gen(1, (B, T, Hq, D), dtype)
