@@ -1,6 +1,12 @@
 """GPU parity: swa_sink_backward (HIP, through the C ABI) against the fp64
 oracle's backward, on the same seeded inputs.  The forward's out and lse come
-from the HIP forward, as they would in training."""
+from the HIP forward, as they would in training.
+
+bf16 bar per gradient: the larger of the N(0,1) bar (5e-2 of rms + |ref|)
+and 1.25x the error of the fp64 model of the kernels' rounding points on the
+same inputs (tests/bf16_model.py) -- on some shapes (D = 64 with a 300-key
+window) those rounding points alone pass 5e-2, and a correct kernel lands on
+the model's error to three digits."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,7 +16,8 @@ import torch
 import oracle
 import sliding_window_learnable_amd as swa
 from sliding_window_learnable_amd import inputs
-from tests.parity import check_grad, to64
+from tests.bf16_model import rounded_backward, scaled_error
+from tests.parity import GRAD_C, check_grad, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +38,14 @@ def bwd_case(gpu, cfg, B, S, Hq, Hkv, D, W, dtype, sink_override=None):
     if sink_override is not None:
         sink = torch.full((Hq,), float(sink_override))
     _, _, got = forward_backward(q.to(gpu), k.to(gpu), v.to(gpu), sink.to(gpu), g.to(gpu), W)
-    ref = oracle.attend_backward(to64(q), to64(k), to64(v), to64(sink), to64(g), W)
-    for name, a, r in zip(("dq", "dk", "dv", "dsink"), got, ref):
-        check_grad(a, r, dtype, name)
+    args = (to64(q), to64(k), to64(v), to64(sink), to64(g), W)
+    ref = oracle.attend_backward(*args)
+    model = rounded_backward(*args) if dtype == torch.bfloat16 else None
+    for n, (name, a, r) in enumerate(zip(("dq", "dk", "dv", "dsink"), got, ref)):
+        c = None
+        if model is not None and name != "dsink":
+            c = max(GRAD_C[dtype], 1.25 * scaled_error(model[n], r))
+        check_grad(a, r, dtype, name, c=c)
     return got, ref
 
 
@@ -47,6 +59,9 @@ CASES = [
     (1, 333, 16, 2, 128, 100),
     (1, 200, 16, 1, 128, 128),     # two query heads per wave (G = 16)
     (2, 130, 32, 2, 64, 64),       # G = 16 at D = 64
+    # windows above 256: four key tiles per dk/dv work-group (two below)
+    (1, 600, 8, 2, 64, 300),
+    (1, 400, 16, 1, 128, 400),     # global, G = 16
 ]
 
 
