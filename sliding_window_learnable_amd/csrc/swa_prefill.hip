@@ -169,6 +169,16 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         f32x16 sc = mfma32(a[0], cur[0], zero16());
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], cur[ks], sc);
+        // Schedule: four fragment reads ahead of the chained products (left
+        // to itself the compiler issues each read right before its product
+        // and waits for it: 32K prefill 255.9 -> 250.7 us, same outputs).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 7);          // LDS reads
+#pragma unroll
+        for (int ks = 0; ks < D / 16 - 4; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 7);      // a product
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 7);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 7);
         return sc;
     };
     // One-sided masks: the newest tile only needs key <= query, the oldest
@@ -260,6 +270,14 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             o[dt] = mfma32(va[dt][0], p0b, first ? zero16() : o[dt]);
             o[dt] = mfma32(va[dt][1], p1b, o[dt]);
         }
+        // Schedule: the transposing reads of two products ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 8);
+#pragma unroll
+        for (int i = 0; i < D / 16 - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 8);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 8);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 8);
     };
 
     // Output rows of the previous step, as read back for its stores.  A
