@@ -195,6 +195,20 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
     const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
     return __builtin_bit_cast(bf16x4, r);
 }
+// The same read at an LDS byte address.
+__device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t a) {
+    const s16x4 r =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(size_t)a);
+    return __builtin_bit_cast(bf16x4, r);
+}
+// 16 bytes at an LDS byte address.
+__device__ __forceinline__ bf16x8 lds_read16_at(uint32_t a) {
+    return *(__attribute__((address_space(3))) const bf16x8 *)(size_t)a;
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p;
+}
 
 // Buffer descriptor as four scalar dwords (raw buffer, num_records bytes).
 __device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
@@ -242,15 +256,17 @@ __device__ __forceinline__ void lds_poison_wave(T &obj) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
-// The 16 bytes a copy of this lane will write at lds + 16 * lane.
-__device__ __forceinline__ void lds_poison_lane16(const void *lds) {
+// The 16 bytes a copy of this lane will write at LDS address lds + 16 * lane.
+__device__ __forceinline__ void lds_poison_lane16_at(uint32_t lds) {
     if constexpr (kLdsPoison) {
-        const unsigned la =
-            (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds + 16u * (threadIdx.x & 63);
+        const unsigned la = lds + 16u * (threadIdx.x & 63);
         u32x4 p;
         p[0] = p[1] = p[2] = p[3] = kPoisonWord;
         asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(la), "v"(p) : "memory");
     }
+}
+__device__ __forceinline__ void lds_poison_lane16(const void *lds) {
+    lds_poison_lane16_at((unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
 }
 
 // Buffer -> LDS copy (no registers): lane l's 16 bytes at voff land at
@@ -269,14 +285,22 @@ __device__ __forceinline__ void dma16(u32x4 r, const void *lds, uint32_t voff) {
                  "v"(voff), "s"(r)
                  : "memory", "m0");
 }
-// The same copy with the non-temporal cache policy, for data read exactly
-// once in whole cache lines per instruction.
-__device__ __forceinline__ void dma16_nt(u32x4 r, const void *lds, uint32_t voff) {
-    lds_poison_lane16(lds);
-    const unsigned la = __builtin_amdgcn_readfirstlane(
-        (unsigned)(size_t)(__attribute__((address_space(3))) const void *)lds);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(la),
-                 "v"(voff), "s"(r)
+// The same copy to an LDS byte address, with a uniform byte offset added
+// in the scalar offset field (no per-lane add); and with the non-temporal
+// cache policy, for data read exactly once in whole cache lines per
+// instruction.
+__device__ __forceinline__ void dma16_at(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    lds_poison_lane16_at(lds);
+    const unsigned la = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(la),
+                 "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt_at(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    lds_poison_lane16_at(lds);
+    const unsigned la = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds" ::"s"(la),
+                 "v"(voff), "s"(r), "s"(soff)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop

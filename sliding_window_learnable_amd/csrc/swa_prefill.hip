@@ -28,10 +28,11 @@
 // Memory path: every input reaches LDS by buffer->LDS copies (no staging
 // registers): the K and V tiles into the ring, each wave's next 32 query
 // rows into its own Q tile, one step ahead (the query rows are read once, in
-// whole rows per instruction, so their copies are non-temporal).  All tiles
-// are unpadded rows whose 16-byte chunks are XOR-swizzled by row, so the K
-// and Q fragment reads and the transposing V reads are free of bank
-// conflicts.  Once a step's products are issued, the wave moves the next
+// whole rows per instruction, so their copies are non-temporal).  The K and
+// V ring tiles are interleaved so that each lane reads a tile's fragments
+// at one base address plus constants; the Q tiles are unpadded rows whose
+// 16-byte chunks are XOR-swizzled by row.  Every fragment read is free of
+// bank conflicts.  Once a step's products are issued, the wave moves the next
 // step's Q fragments into registers and its Q tile becomes the output
 // staging area: the rows of the P.V products are fed dims in the same
 // permuted order as the score rows are fed keys, so each lane holds 8
@@ -48,10 +49,23 @@ constexpr int kTile = 32;
 constexpr int kMaxTiles = 5;             // ceil((129-1)/32) + 1
 constexpr int kRing = kMaxTiles + 1;     // + the tile being copied
 
+// Ring tiles are interleaved so that every lane reads all its fragments of
+// a tile at one base address plus constants (no per-fragment address
+// arithmetic) and every read is free of bank conflicts:
+//  * K: the 32 rows form four groups of 8 (rows 0-3 with 8-11, 4-7 with
+//    12-15, 16-19 with 24-27, 20-23 with 28-31); within a group, row slot x
+//    (0..7) holds chunk c of its row at 16 x + 128 c, so the 8 rows that
+//    one 16-byte read serves together fall on 8 different 16-byte bank
+//    groups, and the chunks a lane reads are 128 bytes apart;
+//  * V: blocks of 4 rows, chunk c of row r at 16 (r mod 4) + 64 c, so the
+//    16 lanes of a transposing read (4 rows x 2 chunks x 2 halves) fall on
+//    16 different 8-byte bank slots, and the dims a lane reads are 256
+//    bytes per 32 dims apart.
+// Each copy instruction fills 1 KiB of a tile, lane l the 16-byte slot l.
 template <int D, int NW>
 struct RingSmem {
-    bf16 k[kRing][kTile][D];             // K rows, chunks swizzled by row
-    bf16 v[kRing][kTile][D];             // V rows, chunks swizzled by row
+    bf16 k[kRing][kTile][D];             // K tiles, interleaved as above
+    bf16 v[kRing][kTile][D];             // V tiles, interleaved as above
     bf16 q[NW][kTile][D];                // each wave's next 32 query rows, swizzled
 };
 
@@ -95,7 +109,8 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const int lq = lane & 31, hl = lane >> 5;
     const int g = blockIdx.y;
     const int h = g * NW + wave;
-    const int R = ntw + 1;
+    constexpr int R = kRing;                                     // ntw + 1: the launcher checks
+    constexpr uint32_t kTileBytes = kTile * D * 2;
     const float c = kLog2e / sqrtf((float)D);
     // key - query for accumulator register r of a tile starting rel keys
     // after the step's first query: 16(r>>3) + (r&7) + kbias + rel
@@ -113,16 +128,27 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const uint32_t l_lane = hl == 0 ? 4u * lq : kOutOfRange;       // one lane per query
     const float s2 = sink[h] * kLog2e;
 
-    // Copy geometry.  K/V: instruction u of this wave moves RPI rows of the
-    // K (first half of the instructions) or V tile; Q: instruction u moves
-    // rows RPI*u .. of this wave's 32 query rows.  Lane l's 16 bytes land at
-    // 16*l past the instruction's first row: row l / CPR, chunk position
-    // l % CPR, which holds source chunk (l % CPR) ^ swz(row).
+    // Copy geometry.  K/V: instruction u of this wave fills 1 KiB (slots
+    // 64 iu .. 64 iu + 63) of the K (first half of the instructions) or V
+    // tile in the interleaved layouts; Q: instruction u moves rows RPI*u ..
+    // of this wave's 32 query rows, lane l's 16 bytes landing at 16*l past
+    // the instruction's first row: row l / CPR, chunk position l % CPR,
+    // which holds source chunk (l % CPR) ^ swz(row).
     uint32_t kv_off[IPW];
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-        const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
-        kv_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
+        const int ii = wave * IPW + u, sl = 64 * (ii % (NI / 2)) + lane;
+        int row, ch;
+        if (ii < NI / 2) {                                      // K: groups of 8 rows
+            const int G = sl / (8 * CPR), w = sl % (8 * CPR), x = w % 8;
+            row = 8 * (2 * (G / 2) + x / 4) + 4 * (G % 2) + x % 4;
+            ch = w / 8;
+        } else {                                                // V: blocks of 4 rows
+            const int w = sl % (4 * CPR);
+            row = 4 * (sl / (4 * CPR)) + w % 4;
+            ch = w / 4;
+        }
+        kv_off[u] = row * rs + 16 * ch;
     }
     uint32_t q_off[QI];
 #pragma unroll
@@ -130,30 +156,44 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         const int row = RPI * u + lane / CPR;
         q_off[u] = row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row));
     }
-    // Tile T into its ring slot (rows from r0; past the window: zeros).
+    // LDS byte addresses of the tiles (uniform).
+    const uint32_t k_lds = lds_addr(&sm.k[0][0][0]), v_lds = lds_addr(&sm.v[0][0][0]);
+    const uint32_t q_lds = lds_addr(&sm.q[wave][0][0]);
+    // Tile T into its ring slot (rows from r0; past the window: zeros).  The
+    // tile's offset goes in the copies' scalar offset.
     auto copy_kv = [&](int T) {
         const uint32_t to = (uint32_t)(kTile * T - r0) * rs;
-        const int slot = T % R;
+        const uint32_t so = (uint32_t)(T % R) * kTileBytes;
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
             const int ii = wave * IPW + u;                       // uniform
             const bool is_k = ii < NI / 2;
-            bf16(*tile)[D] = is_k ? sm.k[slot] : sm.v[slot];
-            dma16(is_k ? kd : vd, tile[(ii % (NI / 2)) * RPI], kv_off[u] + to);
+            dma16_at(is_k ? kd : vd, (is_k ? k_lds : v_lds) + so + 1024 * (ii % (NI / 2)), kv_off[u],
+                     to);
         }
     };
     // The 32 query rows from position p into this wave's Q tile.
     auto copy_q = [&](int p) {
         const uint32_t to = (uint32_t)(p - c0) * qrow_bytes;
 #pragma unroll
-        for (int u = 0; u < QI; ++u) dma16_nt(qd, sm.q[wave][RPI * u], q_off[u] + to);
+        for (int u = 0; u < QI; ++u) dma16_nt_at(qd, q_lds + RPI * u * D * 2, q_off[u], to);
     };
 
     // QK contraction order: lane half hl feeds dims [D/2*hl, D/2*hl + D/2),
     // the ks-th MFMA step the 16-byte chunk (D/16)*hl + ks -- for the Q
     // fragments (B operand) and the K rows (A operand) alike.
     const int arow = score_row_key(lq);
-    const int arow_s = swz<D>(arow), qrow_s = swz<D>(lq);
+    const int qrow_s = swz<D>(lq);
+    // This lane's K fragments of a tile: row arow, chunks (D/16)*hl + ks at
+    // one base plus 128 ks (kept opaque, so that the compiler folds the
+    // constants into the reads rather than keeping an address per read).
+    uint32_t k_base;
+    {
+        const int q8 = arow >> 3, x = (arow & 3) + 4 * (q8 & 1);
+        const int G = 2 * (q8 >> 1) + ((arow >> 2) & 1);
+        k_base = k_lds + 16 * D * G + 16 * x + 128 * ((D / 16) * hl);
+        asm volatile("" : "+v"(k_base));
+    }
     auto read_q = [&](bf16x8 (&qf)[D / 16]) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
@@ -161,11 +201,10 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     };
     // S^T of one tile: 32 keys of ring slot `slot` x this wave's 32 queries.
     auto qk = [&](const bf16x8 (&cur)[D / 16], int slot) {
-        const bf16 *krow = sm.k[slot][arow];
+        const uint32_t ka = k_base + slot * kTileBytes;
         bf16x8 a[D / 16];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            a[ks] = *(const bf16x8 *)(krow + 8 * (((D / 16) * hl + ks) ^ arow_s));
+        for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 128 * ks);
         f32x16 sc = mfma32(a[0], cur[0], zero16());
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], cur[ks], sc);
@@ -248,20 +287,24 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     // reads: in each 16-lane group lane j names 4 dims of key row j/4 --
     // dims 4*pm(j&3) of the group's 16-dim span, pm = (0, 2, 1, 3), which is
     // the permutation within 16 rows -- and lane i receives dim i of the 4 rows.
+    // In the V tile (blocks of 4 rows) lane i's rows r1 = 16 kk + 8 hl + tr_j/4
+    // and r1 + 4 and its dims 32 dt + tr_d .. + 3 lie at one base plus
+    // 32 D kk (16 rows), 8 D (4 rows) and 256 dt (32 dims).
     const int tr_j = lane & 15;
     const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (((tr_j & 1) << 1) | ((tr_j >> 1) & 1));
+    uint32_t v_base = v_lds + 16 * D * hl + 16 * (tr_j >> 2) + 64 * (tr_d >> 3) + 8 * ((tr_d >> 2) & 1);
+    asm volatile("" : "+v"(v_base));
     auto pv = [&](f32x16 (&o)[D / 32], const bf16x8 &p0b, const bf16x8 &p1b, int slot,
                   bool first) {
-        const bf16(*vt)[D] = sm.v[slot];
+        const uint32_t va0 = v_base + slot * kTileBytes;
         bf16x8 va[D / 32][2];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-            const int d = 32 * dt + tr_d, cc = d >> 3, half = (d >> 2) & 1;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
-                const bf16x4 lo = lds_read_tr(&vt[r1][8 * (cc ^ swz<D>(r1)) + 4 * half]);
-                const bf16x4 hi4 = lds_read_tr(&vt[r2][8 * (cc ^ swz<D>(r2)) + 4 * half]);
+                const uint32_t a = va0 + 256 * dt + 32 * D * kk;
+                const bf16x4 lo = lds_read_tr_at(a);
+                const bf16x4 hi4 = lds_read_tr_at(a + 8 * D);
                 va[dt][kk] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
             }
         }
@@ -329,6 +372,9 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
             pv(o, pa, pbb, (T >= 0 ? T : T1) % R, t == 0);
             if (t + 1 < kMaxTiles) {
                 if (T - 1 < 0) {
+                    // A real branch, taken only in a sequence's first four
+                    // steps (as selects it costs 16 instructions per tile).
+                    asm volatile("" ::: "memory");
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s_next[r] = -INFINITY;
                 } else if (t + 1 == kMaxTiles - 1 || (t + 1 == kMaxTiles - 2 && W < 4 * kTile)) {
@@ -479,6 +525,7 @@ namespace {
 template <int D, int NW>
 hipError_t launch_ring(const PrefillArgs &a, hipStream_t stream) {
     const int ntw = (a.window - 1 + kTile - 1) / kTile + 1;
+    if (ntw + 1 != kRing) return hipErrorInvalidValue;        // a window of 5 tiles, one more in flight
     const int cap_tiles = prefill_chunk_cap(a.Hq, a.Hkv, a.D, ntw) / kTile;
     if (a.cu_seqlens != nullptr) {
         // Packed batch: at most (total + 31 B) / 32 tiles in all; split them
