@@ -16,8 +16,9 @@
 //
 // Pipeline: key tiles are copied from memory straight into an LDS ring of
 // four slots (buffer->LDS copies, no staging registers), three tiles ahead,
-// as rows whose 16-byte chunks are swizzled by row: K rows feed the A
-// operand of S^T directly and V^T is read with transposing LDS reads.  In
+// interleaved so that a lane reads all its fragments of a tile at one base
+// address plus constants, free of bank conflicts: K rows feed the A operand
+// of S^T directly and V^T is read with transposing LDS reads.  In
 // iteration t a wave issues the S^T products of tile t+1 before the
 // softmax of tile t (so the matrix unit and the vector unit work at once),
 // then the PV products of tile t; the copies of tile t+3 go to the slot
@@ -47,10 +48,15 @@ constexpr int kSlots = 4;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr float kBig = 256.0f;           // 2^kRescaleSlack
 
+// K tiles: rows in four groups of 8 (rows 0-3 with 8-11, 4-7 with 12-15,
+// 16-19 with 24-27, 20-23 with 28-31), row slot x of a group holding chunk
+// c of its row at 16 x + 128 c.  V tiles: blocks of 4 rows, chunk c of row
+// r at 16 (r mod 4) + 64 c.  Each copy instruction fills 1 KiB of a tile,
+// lane l the 16-byte slot l.
 template <int D>
 struct StreamSmem {
-    bf16 k[kSlots][kTile][D];            // K rows, chunks swizzled by row
-    bf16 v[kSlots][kTile][D];            // V rows, chunks swizzled by row
+    bf16 k[kSlots][kTile][D];            // K tiles, interleaved as above
+    bf16 v[kSlots][kTile][D];            // V tiles, interleaved as above
 };
 
 // BLK: also write, per (query head, 32-row block, key block of 32 rk keys),
@@ -145,12 +151,24 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     constexpr int NI = 2 * kTile / RPI;                // instructions per tile
     constexpr int IPW = NI / NW;
     static_assert(IPW >= 1 && IPW * NW == NI, "copy split");
+    constexpr uint32_t kTileBytes = kTile * D * 2;
     uint32_t dma_off[IPW];
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-        const int row = ((wave * IPW + u) % (NI / 2)) * RPI + lane / CPR;
-        dma_off[u] = row * rs + 16 * ((lane % CPR) ^ swz<D>(row));
+        const int ii = wave * IPW + u, sl = 64 * (ii % (NI / 2)) + lane;
+        int row, ch;
+        if (ii < NI / 2) {                             // K: groups of 8 rows
+            const int Gr = sl / (8 * CPR), w = sl % (8 * CPR), x = w % 8;
+            row = 8 * (2 * (Gr / 2) + x / 4) + 4 * (Gr % 2) + x % 4;
+            ch = w / 8;
+        } else {                                       // V: blocks of 4 rows
+            const int w = sl % (4 * CPR);
+            row = 4 * (sl / (4 * CPR)) + w % 4;
+            ch = w / 4;
+        }
+        dma_off[u] = row * rs + 16 * ch;
     }
+    const uint32_t k_lds = lds_addr(&sm.k[0][0][0]), v_lds = lds_addr(&sm.v[0][0][0]);
     // When the whole key range of the sequence fits one descriptor's 32-bit
     // range, the descriptors are built once and a tile's offset rides in the
     // per-lane offset (range-checked, so rows past the end still land as
@@ -173,16 +191,30 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         for (int u = 0; u < IPW; ++u) {
             const int ii = wave * IPW + u;             // uniform
             const bool is_k = ii < NI / 2;
-            bf16(*tile)[D] = is_k ? sm.k[slot] : sm.v[slot];
-            dma16(is_k ? kr : vr, tile[(ii % (NI / 2)) * RPI], dma_off[u] + to_b);
+            dma16_at(is_k ? kr : vr,
+                     (is_k ? k_lds : v_lds) + slot * kTileBytes + 1024 * (ii % (NI / 2)), dma_off[u],
+                     to_b);
         }
     };
     auto dma_wait = [&](bool newer) {
         if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
-    const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
+    // This lane's fragment addresses in ring slot 0 (opaque, so that the
+    // constants stay immediates of the reads): K row score_row_key(lq),
+    // chunks 2 ks + hl at one base plus 256 ks; V^T rows r1 = 16 kk + 8 hl +
+    // tr_j/4 and r1 + 4, dims 32 dt + tr_d .. + 3, at one base plus 32 D kk,
+    // 8 D and 256 dt.
+    const int arow_r = score_row_key(lq);
     const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+    uint32_t k_base, v_base;
+    {
+        const int q8 = arow_r >> 3, x = (arow_r & 3) + 4 * (q8 & 1);
+        const int Gr = 2 * (q8 >> 1) + ((arow_r >> 2) & 1);
+        k_base = k_lds + 16 * D * Gr + 16 * x + 128 * hl;
+        v_base = v_lds + 16 * D * hl + 16 * (tr_j >> 2) + 64 * (tr_d >> 3) + 8 * ((tr_d >> 2) & 1);
+        asm volatile("" : "+v"(k_base), "+v"(v_base));
+    }
 
     for (int hh = wave; hh < G; hh += NW) {
         const int h = g * G + hh;
@@ -208,10 +240,10 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
         for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
         auto qk = [&](int slot) {
-            const bf16 *krow = sm.k[slot][arow_r];
+            const uint32_t ka = k_base + slot * kTileBytes;
             bf16x8 a[D / 16];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) a[ks] = *(const bf16x8 *)(krow + 8 * ((2 * ks + hl) ^ arow_s));
+            for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 256 * ks);
             f32x16 sc = mfma32(a[0], qf[0], zero16());
 #pragma unroll
             for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], qf[ks], sc);
@@ -322,17 +354,15 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             const bf16x8 pa = pack8(p, 0), pb = pack8(p, 1);
             // O^T += V^T P^T: A row m = dim 32dt + m, k = key 16kk + 8hl + 0..7,
             // from the V row tile by transposing reads of 4 keys each.
-            const int slot = t % kSlots;
-            const bf16(*vt)[D] = sm.v[slot];
+            const uint32_t va0 = v_base + (t % kSlots) * kTileBytes;
             bf16x8 va[D / 32][2];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const int d = 32 * dt + tr_d, cc = d >> 3, half = (d >> 2) & 1;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int r1 = 16 * kk + 8 * hl + (tr_j >> 2), r2 = r1 + 4;
-                    const bf16x4 lo = lds_read_tr(&vt[r1][8 * (cc ^ swz<D>(r1)) + 4 * half]);
-                    const bf16x4 hi4 = lds_read_tr(&vt[r2][8 * (cc ^ swz<D>(r2)) + 4 * half]);
+                    const uint32_t a = va0 + 256 * dt + 32 * D * kk;
+                    const bf16x4 lo = lds_read_tr_at(a);
+                    const bf16x4 hi4 = lds_read_tr_at(a + 8 * D);
                     va[dt][kk] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             }
