@@ -48,10 +48,9 @@ constexpr int kSlots = 4;
 constexpr float kRescaleSlack = 8.0f;    // log2 units
 constexpr float kBig = 256.0f;           // 2^kRescaleSlack
 
-// K tiles: rows in four groups of 8 (rows 0-3 with 8-11, 4-7 with 12-15,
-// 16-19 with 24-27, 20-23 with 28-31), row slot x of a group holding chunk
-// c of its row at 16 x + 128 c.  V tiles: blocks of 4 rows, chunk c of row
-// r at 16 (r mod 4) + 64 c.  Each copy instruction fills 1 KiB of a tile,
+// K tiles: two groups of 16 rows, row r of a group holding chunk c at
+// 16 (r mod 16) + 256 c.  V tiles: blocks of 4 rows, chunk c of row r at
+// 16 (r mod 4) + 64 c.  Each copy instruction fills 1 KiB of a tile,
 // lane l the 16-byte slot l.
 template <int D>
 struct StreamSmem {
@@ -157,10 +156,10 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     for (int u = 0; u < IPW; ++u) {
         const int ii = wave * IPW + u, sl = 64 * (ii % (NI / 2)) + lane;
         int row, ch;
-        if (ii < NI / 2) {                             // K: groups of 8 rows
-            const int Gr = sl / (8 * CPR), w = sl % (8 * CPR), x = w % 8;
-            row = 8 * (2 * (Gr / 2) + x / 4) + 4 * (Gr % 2) + x % 4;
-            ch = w / 8;
+        if (ii < NI / 2) {                             // K: groups of 16 rows
+            const int w = sl % (16 * CPR);
+            row = 16 * (sl / (16 * CPR)) + w % 16;
+            ch = w / 16;
         } else {                                       // V: blocks of 4 rows
             const int w = sl % (4 * CPR);
             row = 4 * (sl / (4 * CPR)) + w % 4;
@@ -202,16 +201,14 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
     };
     // This lane's fragment addresses in ring slot 0 (opaque, so that the
     // constants stay immediates of the reads): K row score_row_key(lq),
-    // chunks 2 ks + hl at one base plus 256 ks; V^T rows r1 = 16 kk + 8 hl +
+    // chunks 2 ks + hl at one base plus 512 ks; V^T rows r1 = 16 kk + 8 hl +
     // tr_j/4 and r1 + 4, dims 32 dt + tr_d .. + 3, at one base plus 32 D kk,
     // 8 D and 256 dt.
     const int arow_r = score_row_key(lq);
     const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
     uint32_t k_base, v_base;
     {
-        const int q8 = arow_r >> 3, x = (arow_r & 3) + 4 * (q8 & 1);
-        const int Gr = 2 * (q8 >> 1) + ((arow_r >> 2) & 1);
-        k_base = k_lds + 16 * D * Gr + 16 * x + 128 * hl;
+        k_base = k_lds + 32 * D * (arow_r / 16) + 16 * (arow_r % 16) + 256 * hl;
         v_base = v_lds + 16 * D * hl + 16 * (tr_j >> 2) + 64 * (tr_d >> 3) + 8 * ((tr_d >> 2) & 1);
         asm volatile("" : "+v"(k_base), "+v"(v_base));
     }
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void stream_attn_kernel(
             const uint32_t ka = k_base + slot * kTileBytes;
             bf16x8 a[D / 16];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 256 * ks);
+            for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 512 * ks);
             f32x16 sc = mfma32(a[0], qf[0], zero16());
 #pragma unroll
             for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], qf[ks], sc);

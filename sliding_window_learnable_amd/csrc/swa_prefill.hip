@@ -52,15 +52,14 @@ constexpr int kRing = kMaxTiles + 1;     // + the tile being copied
 // Ring tiles are interleaved so that every lane reads all its fragments of
 // a tile at one base address plus constants (no per-fragment address
 // arithmetic) and every read is free of bank conflicts:
-//  * K: the 32 rows form four groups of 8 (rows 0-3 with 8-11, 4-7 with
-//    12-15, 16-19 with 24-27, 20-23 with 28-31); within a group, row slot x
-//    (0..7) holds chunk c of its row at 16 x + 128 c, so the 8 rows that
-//    one 16-byte read serves together fall on 8 different 16-byte bank
-//    groups, and the chunks a lane reads are 128 bytes apart;
+//  * K: two groups of 16 rows; row r of a group holds chunk c at
+//    16 (r mod 16) + 256 c, so the 16 rows that a 16-byte read serves in
+//    one cycle (64 banks) fall on 16 different bank groups, and the chunks
+//    a lane reads are 256 bytes apart;
 //  * V: blocks of 4 rows, chunk c of row r at 16 (r mod 4) + 64 c, so the
-//    16 lanes of a transposing read (4 rows x 2 chunks x 2 halves) fall on
-//    16 different 8-byte bank slots, and the dims a lane reads are 256
-//    bytes per 32 dims apart.
+//    32 lanes that an 8-byte transposing read serves in one cycle (4 rows
+//    x 4 chunks x 2 halves) fall on 32 different 8-byte bank slots, and the
+//    dims a lane reads are 256 bytes per 32 dims apart.
 // Each copy instruction fills 1 KiB of a tile, lane l the 16-byte slot l.
 template <int D, int NW>
 struct RingSmem {
@@ -139,10 +138,10 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     for (int u = 0; u < IPW; ++u) {
         const int ii = wave * IPW + u, sl = 64 * (ii % (NI / 2)) + lane;
         int row, ch;
-        if (ii < NI / 2) {                                      // K: groups of 8 rows
-            const int G = sl / (8 * CPR), w = sl % (8 * CPR), x = w % 8;
-            row = 8 * (2 * (G / 2) + x / 4) + 4 * (G % 2) + x % 4;
-            ch = w / 8;
+        if (ii < NI / 2) {                                      // K: groups of 16 rows
+            const int w = sl % (16 * CPR);
+            row = 16 * (sl / (16 * CPR)) + w % 16;
+            ch = w / 16;
         } else {                                                // V: blocks of 4 rows
             const int w = sl % (4 * CPR);
             row = 4 * (sl / (4 * CPR)) + w % 4;
@@ -185,15 +184,10 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
     const int arow = score_row_key(lq);
     const int qrow_s = swz<D>(lq);
     // This lane's K fragments of a tile: row arow, chunks (D/16)*hl + ks at
-    // one base plus 128 ks (kept opaque, so that the compiler folds the
+    // one base plus 256 ks (kept opaque, so that the compiler folds the
     // constants into the reads rather than keeping an address per read).
-    uint32_t k_base;
-    {
-        const int q8 = arow >> 3, x = (arow & 3) + 4 * (q8 & 1);
-        const int G = 2 * (q8 >> 1) + ((arow >> 2) & 1);
-        k_base = k_lds + 16 * D * G + 16 * x + 128 * ((D / 16) * hl);
-        asm volatile("" : "+v"(k_base));
-    }
+    uint32_t k_base = k_lds + 32 * D * (arow / 16) + 16 * (arow % 16) + 256 * ((D / 16) * hl);
+    asm volatile("" : "+v"(k_base));
     auto read_q = [&](bf16x8 (&qf)[D / 16]) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
@@ -204,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         const uint32_t ka = k_base + slot * kTileBytes;
         bf16x8 a[D / 16];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 128 * ks);
+        for (int ks = 0; ks < D / 16; ++ks) a[ks] = lds_read16_at(ka + 256 * ks);
         f32x16 sc = mfma32(a[0], cur[0], zero16());
 #pragma unroll
         for (int ks = 1; ks < D / 16; ++ks) sc = mfma32(a[ks], cur[ks], sc);
