@@ -13,9 +13,10 @@
 // Columns of the MFMA tiles are (token t, head in group) pairs: G*T_q of
 // them per (sequence, KV head), 32 per column tile, so the K/V bytes of a
 // (sequence, KV head) are read from HBM once for all its heads and draft
-// tokens.  Decode is bound by HBM: every wave streams its own keys with the
-// next chunk's loads in flight while the current chunk computes, and waves
-// never wait on each other, so each CU keeps ~16 KiB per wave in flight.
+// tokens.  Decode is bound by HBM: every wave streams its own keys through
+// its own LDS tiles by buffer->LDS copies, the next chunk's copies in flight
+// while the current chunk computes, and waves never wait on each other, so
+// each CU keeps ~16 KiB per wave in flight.
 #include <mutex>
 
 #include "attn_device.h"
@@ -25,8 +26,6 @@ namespace swa {
 namespace {
 
 constexpr int kChunk = 32;          // keys per step (one S^T tile)
-constexpr int kVtPad = 4;           // V^T row padding: conflict-free transposed writes
-constexpr int kKtPad = 8;           // K row padding: conflict-free fragment reads
 constexpr int kWavesPerWG = 4;      // independent waves per work-group
 
 // Mode RING: keys are ring slots 0..W-1 of [B, Hkv, W, D]; with base =
@@ -37,23 +36,33 @@ constexpr int kWavesPerWG = 4;      // independent waves per work-group
 // visible to token t when <= S_kv-T+t.
 //
 // One wave = one work item (column tile ct, split, KV head g, sequence b):
-// it streams the item's keys in 32-key chunks, the next chunk's K
-// fragments and V rows being loaded into registers while the current chunk
-// computes.  Per chunk: S^T = K Q^T (K fragments straight from HBM into the
-// A operand), mask, online softmax (running max seeded with the sink in
-// RING mode, raised lazily), V^T staged through this wave's own LDS tile,
-// O^T += V^T P^T.  Waves never synchronise with each other.
+// it streams the item's keys in 32-key chunks through its own K and V LDS
+// tiles.  Per chunk: the K fragments are read once the chunk's K copy has
+// landed and the K tile takes the next chunk's copy; S^T = K Q^T, mask,
+// online softmax (running max seeded with the sink in RING mode, raised
+// lazily); then the V^T fragments (transposing reads) once the V copy has
+// landed, the V tile takes the next chunk's copy, and O^T += V^T P^T.  So
+// each copy has a whole chunk of compute to land in, and the softmax runs
+// while the chunk's V is still arriving.  Waves never synchronise with each
+// other.
 template <int D, bool RING>
 __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ kc, const bf16 *__restrict__ vc,
     const float *__restrict__ sink, bf16 *__restrict__ out, float *__restrict__ lse,
     const int32_t *__restrict__ cache_len, int B, int Hq, int Hkv, int T, int W, int S_kv,
     int kps, int n_ct, int n_splits, float *__restrict__ part, int Wnd) {
-    constexpr int KF = D / 16;                     // Q fragments, K loads per lane
-    constexpr int VPT = D / 64;                    // V items (4 keys x 8 dims) per lane
+    constexpr int KF = D / 16;                     // Q and K fragments per lane
+    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int KU = kChunk * D * 2 / 1024;      // copy instructions per tile
     constexpr float kSlack = 8.0f;                 // log2 units
-    __shared__ __align__(16) bf16 kt_all[kWavesPerWG][kChunk][D + kKtPad];
-    __shared__ __align__(16) bf16 vt_all[kWavesPerWG][D][kChunk + kVtPad];
+    // Each wave's K and V tiles of one chunk, filled by buffer->LDS copies
+    // (lane l of a copy instruction fills the 16-byte slot l of its 1 KiB),
+    // each instruction whole rows (whole cache lines).  K: unpadded rows,
+    // chunk c of row r at c ^ swz(r); V: blocks of 4 rows, chunk c of row r
+    // at 8D (r/4) + 16 (r%4) + 64 c.  The fragment reads (K as rows, V
+    // transposed) are free of bank conflicts, and their addresses are the
+    // same for every chunk.
+    __shared__ __align__(16) bf16 kv_all[kWavesPerWG][2][kChunk][D];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -65,10 +74,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
     const int g = (item / (n_ct * n_splits)) % Hkv;
     const int b = item / (n_ct * n_splits * Hkv);
     const int G = Hq / Hkv;
-    bf16 (*kt)[D + kKtPad] = kt_all[wave];
-    bf16 (*vt)[kChunk + kVtPad] = vt_all[wave];
-    lds_poison_wave(kt_all[wave]);
-    lds_poison_wave(vt_all[wave]);
+    bf16 (*kt)[D] = kv_all[wave][0];              // the K tile, also the output staging area
+    lds_poison_wave(kv_all[wave]);
     const float c = kLog2e / sqrtf((float)D);
 
     // This lane's column: token t, query head h.
@@ -105,8 +112,8 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
         vbase = vc + (((size_t)b * S_kv + k_begin) * Hkv + g) * D;
         kv_bytes = (uint32_t)(n_keys - 1) * rs + D * 2;
     }
-    const rsrc_t kr = make_rsrc(kbase, kv_bytes);            // keys past the item read zeros
-    const rsrc_t vr = make_rsrc(vbase, kv_bytes);
+    const u32x4 kr = sgpr_rsrc(kbase, kv_bytes);             // keys past the item read zeros
+    const u32x4 vr = sgpr_rsrc(vbase, kv_bytes);
     const int n_chunks = (n_keys + kChunk - 1) / kChunk;
 
     // Q fragments (B operand of S^T): lane half hl feeds dims [D/2*hl, D/2*hl + D/2).
@@ -116,29 +123,35 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
 #pragma unroll
         for (int ks = 0; ks < KF; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 8 * ks);
     }
-    // K is loaded whole rows at a time (16 lanes per 256-byte row, so every
-    // load instruction covers full cache lines; K and V are read once, so the
-    // loads are non-temporal) and turned into MFMA
-    // fragments through the wave's LDS tile.  Load u, lane i: 16-byte piece
-    // e = 64u + i of the chunk, row e / (D/8), column piece e % (D/8).
-    bf16x8 kf[KF];                                   // K rows (16-byte pieces) of the current chunk
-    bf16x8 vq[VPT][4];                               // V rows (4 keys x 8 dims) of the current chunk
-    auto load_k = [&](int k0) {
+    // Copy geometry of a chunk: K instruction u moves rows RPI u .. RPI u +
+    // RPI - 1, lane l's 16 bytes holding source chunk (l % CPR) ^ swz(row);
+    // V instruction u fills slots 64 u .. 64 u + 63 of the V tile (64/CPR
+    // rows), the source offset a per-lane part plus a uniform one.  Whole
+    // cache lines are read per instruction (both are read once: the copies
+    // are non-temporal).
+    constexpr int RPI = 64 / CPR;                  // K rows per copy instruction
+    const uint32_t v_lane = (4 * (lane / (4 * CPR)) + lane % 4) * rs + 16 * ((lane % (4 * CPR)) / 4);
+    const uint32_t k_lds = lds_addr(&kv_all[wave][0][0][0]), v_lds = lds_addr(&kv_all[wave][1][0][0]);
+    auto copy_k = [&](int k0) {
 #pragma unroll
-        for (int u = 0; u < KF; ++u) {
-            const int e = 64 * u + lane;
-            kf[u] = buf_load16_nt(kr, (e / (D / 8)) * rs + 16 * (e % (D / 8)), (uint32_t)k0 * rs);
+        for (int u = 0; u < KU; ++u) {
+            const int row = RPI * u + lane / CPR;
+            dma16_nt_at(kr, k_lds + 1024 * u, row * rs + 16 * ((lane % CPR) ^ swz<D>(row)),
+                        (uint32_t)k0 * rs);
         }
     };
-    auto load_v = [&](int k0) {
+    auto copy_v = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int it = lane + 64 * i, kq = it & 7, ch = it >> 3;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vq[i][j] = buf_load16_nt(vr, (4 * kq + j) * rs + 16 * ch, (uint32_t)k0 * rs);
-        }
+        for (int u = 0; u < KU; ++u)
+            dma16_nt_at(vr, v_lds + 1024 * u, v_lane, (uint32_t)(k0 + (64 / CPR) * u) * rs);
     };
+    // Fragment addresses: K row score_row_key(lq), chunks (D/16) hl + ks;
+    // V^T rows r1 = 16 kk + 8 hl + tr_j/4 and r1 + 4,
+    // dims 32 dt + tr_d .. + 3, at one base plus 32 D kk, 8 D and 256 dt.
+    const int arow = score_row_key(lq);
+    const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+    uint32_t v_base = v_lds + 16 * D * hl + 16 * (tr_j >> 2) + 64 * (tr_d >> 3) + 8 * ((tr_d >> 2) & 1);
+    asm volatile("" : "+v"(v_base));
 
     float m = -INFINITY;                              // running max (log2 units)
     const float s2 = sink[h] * kLog2e;
@@ -151,61 +164,38 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = zero16();
 
-    // Each register set is refilled with the next chunk as soon as this
-    // chunk has consumed it, so the loads overlap the softmax and PV work.
-    // The refill is unconditional: past the item's keys the loads are out
-    // of the descriptor's range and return zeros without touching memory.
-    // K before V everywhere, so that the S^T products wait only for K.
-    // Neighbouring waves start at different chunks of their keys (the order
-    // of the chunks does not matter to the online softmax), so that the
-    // requests in flight at any moment spread over more address offsets.
+    // Each chunk's fragments are read into registers as soon as it has
+    // landed; then the next chunk's copies go to the same tiles, in flight
+    // for the whole of this chunk's compute.  Neighbouring waves start at
+    // different chunks of their keys (the order of the chunks does not
+    // matter to the online softmax), so that the requests in flight at any
+    // moment spread over more address offsets.
     const int rot = n_chunks > 0 ? item % n_chunks : 0;
-    load_k(kChunk * rot);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(kChunk * rot);
+    if (n_chunks > 0) {
+        copy_k(kChunk * rot);
+        copy_v(kChunk * rot);
+    }
     for (int ci = 0; ci < n_chunks; ++ci) {
         const int cc = ci + rot < n_chunks ? ci + rot : ci + rot - n_chunks;
         const int k0 = kChunk * cc;
-        // The next chunk; after the last, an offset past the item's keys
-        // (the loads then return zeros without touching memory).
-        const int cn = ci + 1 == n_chunks ? n_chunks : (cc + 1 < n_chunks ? cc + 1 : 0);
+        const int cn = cc + 1 < n_chunks ? cc + 1 : 0;
 
-        // Stage this chunk: K rows as they are, V transposed.  The previous
-        // chunk's PV products may still be running, so lds_settle holds the
-        // write data registers until the writes are done; then the same
-        // registers take the next chunk's loads, which stay in flight for
-        // the whole of this chunk's compute.
+        const bool more = ci + 1 < n_chunks;                        // uniform
+        // K of this chunk landed (its V may still be in flight): read the
+        // K fragments, then the K tile takes the next chunk's copy.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KU) : "memory");
+        bf16x8 kf[KF], va[D / 32][2];
 #pragma unroll
-        for (int u = 0; u < KF; ++u) {
-            const int e = 64 * u + lane;
-            *(bf16x8 *)&kt[e / (D / 8)][8 * (e % (D / 8))] = kf[u];
-        }
-        lds_settle(kf);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int it = lane + 64 * i, kq = it & 7, ch = it >> 3;
-            u32x2 w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 x;
-                x[0] = vq[i][0][e];
-                x[1] = vq[i][1][e];
-                x[2] = vq[i][2][e];
-                x[3] = vq[i][3][e];
-                w[e] = __builtin_bit_cast(u32x2, x);
-                *(u32x2 *)&vt[8 * ch + e][4 * kq] = w[e];
-            }
-            lds_settle(w);
-        }
-        load_k(kChunk * cn);
-        load_v(kChunk * cn);
+        for (int ks = 0; ks < KF; ++ks)
+            kf[ks] = *(const bf16x8 *)&kt[arow][8 * (((D / 16) * hl + ks) ^ swz<D>(arow))];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (more) copy_k(kChunk * cn);
 
         // S^T = K Q^T: A row lq is key score_row_key(lq), lane half hl
         // feeds dims [D/2*hl, D/2*hl + D/2) like the Q fragments.
-        const bf16 *krow = &kt[score_row_key(lq)][(D / 2) * hl];
-        f32x16 sc = mfma32(*(const bf16x8 *)krow, qf[0], zero16());
+        f32x16 sc = mfma32(kf[0], qf[0], zero16());
 #pragma unroll
-        for (int ks = 1; ks < KF; ++ks) sc = mfma32(*(const bf16x8 *)(krow + 8 * ks), qf[ks], sc);
+        for (int ks = 1; ks < KF; ++ks) sc = mfma32(kf[ks], qf[ks], sc);
 
         // Visibility mask and chunk max.
         float mx = -INFINITY;
@@ -237,10 +227,25 @@ __global__ __launch_bounds__(64 * kWavesPerWG, 2) void decode_kernel(
             l += p;
         }
         const bf16x8 p0 = pack8(sc, 0), p1 = pack8(sc, 1);
+        // This chunk's V landed (only the next chunk's K copies may be
+        // outstanding): read the V^T fragments, then the V tile takes the
+        // next chunk's copy.
+        if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KU) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint32_t a = v_base + 256 * dt + 32 * D * kk;
+                const bf16x4 lo = lds_read_tr_at(a), hi4 = lds_read_tr_at(a + 8 * D);
+                va[dt][kk] = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (more) copy_v(kChunk * cn);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-            o[dt] = mfma32(*(const bf16x8 *)&vt[32 * dt + lq][8 * hl], p0, o[dt]);
-            o[dt] = mfma32(*(const bf16x8 *)&vt[32 * dt + lq][16 + 8 * hl], p1, o[dt]);
+            o[dt] = mfma32(va[dt][0], p0, o[dt]);
+            o[dt] = mfma32(va[dt][1], p1, o[dt]);
         }
     }
 
