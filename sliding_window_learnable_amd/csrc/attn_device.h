@@ -62,11 +62,6 @@ __device__ __forceinline__ int score_reg_key(int r, int lane) {
     return 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
 }
 
-// Row (0..31 within a 32-row d-tile) of output register r of lane `lane`.
-__device__ __forceinline__ int out_reg_row(int r, int lane) {
-    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &p, int half) {
     bf16x8 b;
 #pragma unroll
@@ -150,16 +145,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ bf16x8 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-__device__ __forceinline__ void buf_store8(bf16x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
-}
 __device__ __forceinline__ void buf_store16(bf16x8 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
-}
-// Streaming load (cache policy "nt") for data read exactly once, in whole
-// cache lines per instruction.
-__device__ __forceinline__ bf16x8 buf_load16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
 }
 // Streaming store (cache policy "nt"): output written once and not read
 // back by this kernel.  Whole 128-byte segments only.
