@@ -137,19 +137,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
         for (int t = 0; t < 3 && t < n_tiles; ++t) stage(T_lo + t, t);
         bf16x8 qf[D / 16], gf[D / 16];
         float dsum_part = 0.0f;
-        {
-            const size_t off = (((size_t)b * S + pq) * Hq + h) * D + 8 * hl;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                qf[ks] = *(const bf16x8 *)(q + off + 16 * ks);
-                gf[ks] = *(const bf16x8 *)(dout + off + 16 * ks);
-                const bf16x8 of = *(const bf16x8 *)(out + off + 16 * ks);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dsum_part = fmaf((float)gf[ks][e], (float)of[e], dsum_part);
-            }
-        }
         const size_t li = ((size_t)b * Hq + h) * S + pq;
         const float lse_i = lse[li];
+        {
+            const size_t off = (((size_t)b * S + pq) * Hq + h) * D + 8 * hl;
+            bf16x8 of[D / 16];
+            // The four loads that share a 128-byte line of a row go out
+            // back to back.
+#pragma unroll
+            for (int k4 = 0; k4 < D / 16; k4 += 4) {
+#pragma unroll
+                for (int ks = k4; ks < k4 + 4; ++ks) qf[ks] = *(const bf16x8 *)(q + off + 16 * ks);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = k4; ks < k4 + 4; ++ks) gf[ks] = *(const bf16x8 *)(dout + off + 16 * ks);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = k4; ks < k4 + 4; ++ks) of[ks] = *(const bf16x8 *)(out + off + 16 * ks);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dsum_part = fmaf((float)gf[ks][e], (float)of[ks][e], dsum_part);
+        }
         const float l2 = lse_i * kLog2e;
         const float Di = dsum_part + __shfl_xor(dsum_part, 32);
         {
