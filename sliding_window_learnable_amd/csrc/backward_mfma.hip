@@ -543,6 +543,387 @@ __global__ __launch_bounds__(2 * NW * 64) void bwd_dkdv_kernel(
     }
 }
 
+// ==================================================================== dk/dv ring
+// For windows up to 129 keys a query tile sees at most five key tiles, so a
+// work-group can own a run of consecutive key tiles and walk the query tiles
+// that see them once, in order, heads innermost.  Key tile j of the run lives
+// in slot (j - k0) mod 6, with two waves per slot as in bwd_dkdv_kernel (S
+// wave: S = Q K^T, P, dV^T += dO^T P; dP wave: dP = dO V^T, dS, dK^T += Q^T dS).
+// A slot's tile is live for the query tiles that see it (at most five) and
+// idle for at least one more; in the first step of that idle span its two
+// waves write dv / dk out as whole rows through an LDS area, copy the slot's
+// next key tile (K for the S wave, V for the dP wave) into the same area and
+// take it into registers.  Each Q / dO tile is then copied once per
+// work-group (plus a tail of nvis - 1 query tiles per run) rather than once
+// for every two key tiles.
+constexpr int kRingSlots = 6;
+
+template <int D>
+struct KvRingSmem {
+    bf16 q[kKvSlots][kTile][D];     // Q rows (swizzled), as in KvSmem
+    bf16 g[kKvSlots][kTile][D];     // dO rows (swizzled)
+    float l2[kKvSlots][kTile];      // lse * log2(e)
+    float dd[kKvSlots][kTile];      // D_i
+    f16x4 px[2][kRingSlots][4][64]; // P of each slot's key tile, S wave -> dP wave
+    bf16 stg[2][kTile][D];          // retiring slot: dv (S wave) / dk rows out, then its next K / V in
+};
+
+template <int D>
+__global__ __launch_bounds__(2 * kRingSlots * 64) void bwd_dkdv_ring_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ l2g, const float *__restrict__ dsum,
+    bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int Hq, int Hkv, int W, int BG, int run) {
+    constexpr int NS = kRingSlots;
+    constexpr int CPR = D / 8;                             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                          // rows per copy instruction
+    constexpr int TI = kTile / RPI;                        // copy instructions per tile
+    constexpr int CW = 4;                                  // copying waves per role
+    constexpr int IPW = TI / CW;                           // ... instructions each
+    static_assert(IPW >= 1 && IPW * CW == TI, "copy split");
+    __shared__ __align__(16) KvRingSmem<D> sm;
+    lds_poison_all(sm);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool role_s = wave < NS;                         // S/P/dV wave, else dP/dS/dK
+    const int slot = role_s ? wave : wave - NS;
+    const bool copier = slot < CW;
+    const int lq = lane & 31, hl = lane >> 5;
+    const int bg = blockIdx.x % BG;
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int G = Hq / Hkv;
+    const float c = kLog2e / sqrtf((float)D);
+    const float scale = 1.0f / sqrtf((float)D);
+    const int nQT = (S + kTile - 1) / kTile;
+    const int k0 = (blockIdx.x / BG) * run;                // this run's key tiles: [k0, k_end)
+    const int k_end = min(nQT, k0 + run);
+    const int nvis = (W + kTile - 2) / kTile + 1;          // query tiles that see one key tile
+    const int t_end = min(nQT - 1, k_end - 1 + nvis - 1);  // last query tile of the walk
+    const uint32_t rs = (uint32_t)Hkv * D * 2;
+    const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
+
+    int kt = k0 + slot;                                    // this slot's key tile (k_end: none)
+    auto active = [&](int qt) __attribute__((always_inline)) { return kt < k_end && qt >= kt && (qt - kt) * kTile < W + kTile - 1; };
+
+    // The first key tile of the slot as B operands (lane = key, dims 16ks + 8hl).
+    bf16x8 kvf[D / 16];
+    {
+        const int j0 = kt * kTile;
+        const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTile, S - j0)));
+        const size_t base = (((size_t)b * S + min(j0, S - 1)) * Hkv + g) * D;
+        const rsrc_t r = make_rsrc((role_s ? k : v) + base, (uint32_t)rows * rs);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            kvf[ks] = buf_load16(r, lq * rs + 2 * (16 * ks + 8 * hl), 0);
+    }
+    f32x16 acc[D / 32];                                    // dV^T (S waves) or dK^T
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+
+    const int N = (t_end - k0 + 1) * G;                    // pairs (query tile, head), heads inner
+    // Operand addresses.  With 256-byte rows, chunk (2ks + hl) ^ s of a row
+    // (s = swz(row)) sits at byte 16((hl ^ s) & 1) + 32(ks ^ (s >> 1)): one
+    // per-lane base XOR 32ks.  Transposing reads of rows r1 = 16kk + 8hl +
+    // j4 and r1 + 4 (j4 = tr_j / 4), dims 32dt + tr_d: bytes 4096kk + base_rr
+    // XOR 64dt, the row's swizzle putting j4 in bits 6-7.  The bases are
+    // made opaque where they are used, so that the compiler recomputes the
+    // few XORs instead of keeping every read address live in the loop.
+    static_assert(D == 128, "ring kernel address scheme: 256-byte rows");
+    const int arow_r = score_row_key(lq), arow_s = swz<D>(arow_r);
+    const uint32_t sc_off = 256 * arow_r + 16 * ((hl ^ arow_s) & 1) + 32 * (arow_s >> 1);
+    const uint32_t role_a = lds_addr(role_s ? &sm.q[0][0][0] : &sm.g[0][0][0]);  // A of S / dP
+    const uint32_t role_t = lds_addr(role_s ? &sm.g[0][0][0] : &sm.q[0][0][0]);  // transposed A
+    constexpr uint32_t kTileB = kTile * D * 2;
+    auto scores = [&](int bi) __attribute__((always_inline)) {
+        uint32_t base = role_a + sc_off;
+        asm volatile("" : "+v"(base));
+        base += bi * kTileB;
+        f32x16 x = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) x = mfma32(lds_read16_at(base ^ (32u * ks)), kvf[ks], x);
+        // Operand reads two products ahead (few registers at three waves a SIMD).
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 5);
+#pragma unroll
+        for (int ks = 0; ks < D / 16 - 2; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 5);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 5);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 5);
+        return x;
+    };
+    auto softmax = [&](f32x16 &x, int qt, int pbuf, int bi) __attribute__((always_inline)) {
+        const int r0 = qt * kTile, j0 = kt * kTile;
+        const bool masked = qt == kt || (qt * kTile + kTile - 1) - W >= j0;
+        f16x4 *px = sm.px[pbuf][slot][0] + lane;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
+            const f32x4 l2v = *(const f32x4 *)&sm.l2[bi][row];
+            f16x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * u + e;
+                float y = x[r];
+                if (masked) {
+                    const int dij = (r0 + perm_row(r, hl)) - (j0 + lq);
+                    y = (dij >= 0 && dij < W) ? y : -INFINITY;
+                }
+                x[r] = __builtin_amdgcn_exp2f(fmaf(y, c, -l2v[e]));
+                pv[e] = (_Float16)x[r];
+            }
+            px[64 * u] = pv;
+        }
+    };
+    const int tr_j = lane & 15, tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_j & 3);
+    uint32_t tr_off[2];
+    {
+        const int j4 = tr_j >> 2, c0 = tr_d >> 3, half = (tr_d >> 2) & 1;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 8 * hl + j4 + 4 * rr;                 // kk = 0
+            tr_off[rr] = 256 * r + 16 * (c0 ^ (swz<D>(r) & 3)) + 8 * half + 64 * (swz<D>(r) >> 2);
+        }
+    }
+    auto accumulate = [&](const bf16x8 &xa, const bf16x8 &xb, int bi) __attribute__((always_inline)) {
+        uint32_t b0 = role_t + tr_off[0], b1 = role_t + tr_off[1];
+        asm volatile("" : "+v"(b0), "+v"(b1));
+        b0 += bi * kTileB;
+        b1 += bi * kTileB;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const uint32_t a0 = b0 ^ (64u * dt), a1 = b1 ^ (64u * dt);
+            bf16x8 a[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x4 lo = lds_read_tr_at(a0 + 4096u * kk);
+                const bf16x4 hi = lds_read_tr_at(a1 + 4096u * kk);
+                a[kk] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            acc[dt] = mfma32(a[0], xa, acc[dt]);
+            acc[dt] = mfma32(a[1], xb, acc[dt]);
+        }
+        // Transposing reads (two per operand) one product ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 6);
+#pragma unroll
+        for (int i = 0; i < D / 16 - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 6);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 6);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 6);
+    };
+
+    // Q / dO rows of the pairs in order (S waves Q and lse*log2(e), dP waves
+    // dO and D); waves of slots 0..CW-1 copy IPW instructions each, slot 0
+    // also the 128-byte row vector.
+    const bf16 *tsrc = role_s ? q : dout;
+    const float *vsrc = role_s ? l2g : dsum;
+    uint32_t dma_off[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+        const int row = (slot * IPW + u) * RPI + lane / CPR;
+        dma_off[u] = row * qrow_bytes + 16 * ((lane % CPR) ^ swz<D>(row));
+    }
+    int ld_t = k0, ld_h = 0;                               // next pair to copy
+    auto stage = [&](int sl) __attribute__((always_inline)) {
+        if (copier) {
+            const int r0 = ld_t * kTile;
+            const int rows = min(kTile, S - r0);
+            const int hq = g * G + ld_h;
+            const size_t base = (((size_t)b * S + r0) * Hq + hq) * D;
+            const u32x4 r = sgpr_rsrc(tsrc + base, (uint32_t)(rows - 1) * qrow_bytes + D * 2);
+            bf16(*tile)[D] = role_s ? sm.q[sl] : sm.g[sl];
+#pragma unroll
+            for (int u = 0; u < IPW; ++u) dma16(r, tile[(slot * IPW + u) * RPI], dma_off[u]);
+            if (slot == 0) {
+                const u32x4 rv = sgpr_rsrc(vsrc + ((size_t)b * Hq + hq) * S + r0, (uint32_t)rows * 4);
+                if (lane < kTile / 4) dma16(rv, role_s ? sm.l2[sl] : sm.dd[sl], 16 * lane);
+            }
+        }
+        if (++ld_h == G) {
+            ld_h = 0;
+            ++ld_t;
+        }
+    };
+    // Wait for this wave's copies except those of the current step (newer).
+    auto dma_wait = [&](bool newer) __attribute__((always_inline)) {
+        if (!newer || !copier) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (slot == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+    };
+
+    // Retire the slot's key tile: dv (S wave) or dk rows through the LDS
+    // area st, stored as whole rows; then, with more = true and a next tile
+    // in the run, copy that tile (K or V) into the same area.  Returns with
+    // the stores complete (their data registers held until then) and the
+    // copy in flight.  In the walk one slot retires per query tile, through
+    // the role's area of sm.stg.
+    bf16(*stg)[D] = sm.stg[role_s ? 0 : 1];
+    auto retire_tile = [&](bf16(*st)[D], bool more) __attribute__((always_inline)) {
+        // Lane-derived addresses computed here, not kept live through the walk.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lq = ln & 31, hl = ln >> 5;
+        const int lane = ln;
+        const int j0 = kt * kTile;
+        const float f = role_s ? 1.0f : scale;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            u32x2 w[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                bf16x4 xo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xo[e] = (bf16)(acc[dt][4 * jj + e] * f);
+                w[jj] = __builtin_bit_cast(u32x2, xo);
+                const int cidx = 4 * dt + jj;
+                *(u32x2 *)&st[lq][8 * (cidx ^ swz<D>(lq)) + 4 * hl] = w[jj];
+            }
+            lds_settle(w);
+        }
+        // Rows out in two halves, each held until its stores are complete
+        // (fewer registers live at once); the next tile's copy after them.
+        const int rows = __builtin_amdgcn_readfirstlane(min(kTile, S - j0));
+        const rsrc_t rd = make_rsrc((role_s ? dv : dk) + (((size_t)b * S + j0) * Hkv + g) * D,
+                                    (uint32_t)rows * rs);
+        kt += NS;
+        const bool copy_next = more && kt < k_end;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            bf16x8 y[TI / 2];
+#pragma unroll
+            for (int u = 0; u < TI / 2; ++u) {
+                const int r = RPI * (TI / 2 * hf + u) + lane / CPR, cidx = lane % CPR;
+                y[u] = *(const bf16x8 *)&st[r][8 * (cidx ^ swz<D>(r))];
+            }
+#pragma unroll
+            for (int u = 0; u < TI / 2; ++u)
+                buf_store16(y[u], rd, (uint32_t)(RPI * (TI / 2 * hf + u) + lane / CPR) * rs +
+                                          16 * (lane % CPR), 0);
+            if (hf == 1 && copy_next) {
+                // The read-back is complete (the stores consumed it).
+                const int j1 = kt * kTile;
+                const int rows1 = __builtin_amdgcn_readfirstlane(min(kTile, S - j1));
+                const u32x4 r = sgpr_rsrc((role_s ? k : v) + (((size_t)b * S + j1) * Hkv + g) * D,
+                                          (uint32_t)(rows1 - 1) * rs + D * 2);
+                const uint32_t st_lds = __builtin_amdgcn_readfirstlane(lds_addr(&st[0][0]));
+#pragma unroll
+                for (int u = 0; u < TI; ++u) {
+                    const int row = RPI * u + lane / CPR;
+                    dma16_at(r, st_lds + 1024u * u, row * rs + 16 * ((lane % CPR) ^ swz<D>(row)), 0);
+                }
+                hold_until_done<TI>(y);
+            } else {
+                hold_until_done<0>(y);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+    };
+    // The slot's key tile from stg into the B-operand registers (after its copy landed).
+    auto take_tile = [&]() __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lq = ln & 31, hl = ln >> 5;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            kvf[ks] = *(const bf16x8 *)&stg[lq][8 * ((2 * ks + hl) ^ swz<D>(lq))];
+    };
+
+    for (int n = 0; n < 3 && n < N; ++n) stage(n);       // overlaps the K/V row loads
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) retire(kvf[ks]);
+    dma_wait(false);
+    lds_barrier();
+
+    bf16x8 pa, pb;                                         // P of pair n (S waves)
+    if (role_s && active(k0)) {
+        f32x16 x = scores(0);
+        softmax(x, k0, 0, 0);
+        pa = pack8(x, 0);
+        pb = pack8(x, 1);
+    }
+    lds_barrier();
+
+    // Step n: the slot's retirement if pair n is the first after its tile's
+    // last; copy pair n+3 into slot (n+3)%4; S waves: P of pair n+1, dV of
+    // pair n; dP waves: dS and dK of pair n; wait for pair n+2's copy.
+    // Retirement at the start of step n if pair n is the first after the
+    // slot's last: the next tile is taken now when pair n+1 (the S wave's
+    // look-ahead) already needs it, else after this step's wait.
+    auto maybe_retire = [&](int t_cur, int h_cur, int t_next, int n) __attribute__((always_inline)) {
+        bool take_late = false;
+        if (h_cur == 0 && kt < k_end && t_cur == kt + nvis) {
+            retire_tile(stg, true);
+            if (kt < k_end) {
+                if (role_s && n + 1 < N && active(t_next)) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    take_tile();
+                } else {
+                    take_late = true;
+                }
+            }
+        }
+        return take_late;
+    };
+    int t_cur = k0, h_cur = 0;                             // pair n
+    if (role_s) {
+        for (int n = 0; n < N; ++n) {
+            const int bi = n % kKvSlots, bn = (n + 1) % kKvSlots;
+            const int t_next = h_cur + 1 == G ? t_cur + 1 : t_cur;
+            const bool take_late = maybe_retire(t_cur, h_cur, t_next, n);
+            const bool copy = n + 3 < N;
+            if (copy) stage((n + 3) % kKvSlots);
+            // dV of pair n first, then P of pair n+1, kept apart so that the
+            // two products' operand reads are never live together.
+            if (active(t_cur)) accumulate(pa, pb, bi);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n + 1 < N && active(t_next)) {
+                f32x16 x = scores(bn);
+                softmax(x, t_next, (n + 1) & 1, bn);
+                pa = pack8(x, 0);
+                pb = pack8(x, 1);
+            }
+            dma_wait(copy);                                // also the retirement's tile copy
+            if (take_late) take_tile();
+            lds_barrier();                                 // step n done
+            t_cur = t_next;
+            h_cur = h_cur + 1 == G ? 0 : h_cur + 1;
+        }
+    } else {
+        for (int n = 0; n < N; ++n) {
+            const int bi = n % kKvSlots;
+            const int t_next = h_cur + 1 == G ? t_cur + 1 : t_cur;
+            const bool take_late = maybe_retire(t_cur, h_cur, t_next, n);
+            const bool copy = n + 3 < N;
+            if (copy) stage((n + 3) % kKvSlots);
+            if (active(t_cur)) {
+                f32x16 x = scores(bi);
+                const f16x4 *px = sm.px[n & 1][slot][0] + lane;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int row = 16 * (u >> 1) + 8 * hl + 4 * (u & 1);
+                    const f32x4 ddv = *(const f32x4 *)&sm.dd[bi][row];
+                    const f16x4 pv = px[64 * u];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[4 * u + e] = pv[e] * (x[4 * u + e] - ddv[e]);
+                }
+                accumulate(pack8(x, 0), pack8(x, 1), bi);
+            }
+            dma_wait(copy);
+            if (take_late) take_tile();
+            lds_barrier();                                 // step n done
+            t_cur = t_next;
+            h_cur = h_cur + 1 == G ? 0 : h_cur + 1;
+        }
+    }
+    // Tiles still live at the end of the walk (up to one per slot) retire
+    // together, each wave through its own 32 x D area of the now idle LDS.
+    lds_barrier();
+    static_assert(sizeof(sm) >= (size_t)2 * NS * kTile * D * 2, "final staging");
+    if (kt < k_end)
+        retire_tile(reinterpret_cast<bf16(*)[D]>(reinterpret_cast<char *>(&sm)) + wave * kTile, false);
+}
+
 template <int D, int NW>
 hipError_t launch_dq(const BackwardArgs &a, hipStream_t stream) {
     const int BG = a.B * a.Hkv;
@@ -574,8 +955,26 @@ hipError_t launch_dkdv_nw(const BackwardArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Key tiles per ring work-group: enough work-groups to give every CU one,
+// at least one tile per slot.
+hipError_t launch_dkdv_ring(const BackwardArgs &a, hipStream_t stream) {
+    constexpr int D = 128;
+    const int BG = a.B * a.Hkv;
+    const int nKT = (a.S + kTile - 1) / kTile;
+    const long want = 256;
+    const int run = (int)max((long)kRingSlots, ((long)nKT * BG + want - 1) / want);
+    const int nrun = (nKT + run - 1) / run;
+    hipLaunchKernelGGL((bwd_dkdv_ring_kernel<D>), dim3((unsigned)((long)BG * nrun)),
+                       dim3(2 * kRingSlots * 64), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                       (const bf16 *)a.v, (const bf16 *)a.dout, a.ws_l2, a.ws_dsum, (bf16 *)a.dk,
+                       (bf16 *)a.dv, a.S, a.Hq, a.Hkv, a.window, BG, run);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_dkdv(const BackwardArgs &a, hipStream_t stream) {
+    if constexpr (D == 128)
+        if (a.window <= 129) return launch_dkdv_ring(a, stream);
     return a.window <= 256 ? launch_dkdv_nw<D, 2>(a, stream) : launch_dkdv_nw<D, 4>(a, stream);
 }
 

@@ -59,6 +59,12 @@ CASES = [
     (1, 333, 16, 2, 128, 100),
     (1, 200, 16, 1, 128, 128),     # two query heads per wave (G = 16)
     (2, 130, 32, 2, 64, 64),       # G = 16 at D = 64
+    # key-tile ring (D = 128, window <= 129): one query head per KV head, so
+    # a slot's next tile is needed in the step it retires; two heads; the
+    # widest ring window; a two-tile window
+    (1, 700, 4, 4, 128, 128),
+    (1, 520, 4, 2, 128, 129),
+    (2, 450, 8, 8, 128, 33),
     # windows above 256: four key tiles per dk/dv work-group (two below)
     (1, 600, 8, 2, 64, 300),
     (1, 400, 16, 1, 128, 400),     # global, G = 16
