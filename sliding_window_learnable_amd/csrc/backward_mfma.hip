@@ -603,7 +603,9 @@ __global__ __launch_bounds__(2 * kRingSlots * 64) void bwd_dkdv_ring_kernel(
     const uint32_t qrow_bytes = (uint32_t)Hq * D * 2;
 
     int kt = k0 + slot;                                    // this slot's key tile (k_end: none)
-    auto active = [&](int qt) __attribute__((always_inline)) { return kt < k_end && qt >= kt && (qt - kt) * kTile < W + kTile - 1; };
+    auto active = [&](int qt) __attribute__((always_inline)) {
+        return kt < k_end && qt >= kt && (qt - kt) * kTile < W + kTile - 1;
+    };
 
     // The first key tile of the slot as B operands (lane = key, dims 16ks + 8hl).
     bf16x8 kvf[D / 16];
@@ -844,12 +846,11 @@ __global__ __launch_bounds__(2 * kRingSlots * 64) void bwd_dkdv_ring_kernel(
     }
     lds_barrier();
 
-    // Step n: the slot's retirement if pair n is the first after its tile's
-    // last; copy pair n+3 into slot (n+3)%4; S waves: P of pair n+1, dV of
-    // pair n; dP waves: dS and dK of pair n; wait for pair n+2's copy.
-    // Retirement at the start of step n if pair n is the first after the
-    // slot's last: the next tile is taken now when pair n+1 (the S wave's
-    // look-ahead) already needs it, else after this step's wait.
+    // Step n: the slot retires its tile if pair n is the first after the
+    // tile's last (the next tile is taken at once when pair n+1, the S wave's
+    // look-ahead, already needs it, else after this step's wait); copy pair
+    // n+3 into slot (n+3)%4; S waves: dV of pair n, P of pair n+1; dP waves:
+    // dS and dK of pair n; wait for pair n+2's copy.
     auto maybe_retire = [&](int t_cur, int h_cur, int t_next, int n) __attribute__((always_inline)) {
         bool take_late = false;
         if (h_cur == 0 && kt < k_end && t_cur == kt + nvis) {
