@@ -122,3 +122,34 @@ def test_backward_32k_slices_and_sink_identity(gpu):
     dot = (g.double() * out.double()).sum(-1).permute(0, 2, 1)              # B Hq S
     expect = -(torch.exp(sink.double()[None, :, None] - lse.double()) * dot).sum(dim=(0, 2))
     check_grad(ds, to64(expect), torch.float32, "dsink", c=1e-4)
+
+
+def test_backward_262144_slices(gpu):
+    """Window-128 backward at S=262144 (B=1, Hq=64, Hkv=8, D=128), where the
+    dk/dv work-groups walk runs of 256 key tiles (8192 positions) rather than
+    the 32 of the 32K workload.  Two slices against the oracle run on them:
+    one across the boundary between the third and fourth runs (position
+    24576) and the last 640 rows of the sequence; a slice preceded by W-1
+    context tokens has every row's window complete, and keys at least W-1
+    before its end receive all their queries."""
+    B, S, Hq, Hkv, D, W = 1, 262144, 64, 8, 128, 128
+    print("backward 262144", flush=True)
+    q, k, v, sink = inputs.attention_inputs(9, 0, B, S, S, Hq, Hkv, D, torch.bfloat16, "cuda")
+    g = inputs.upstream_grad(9, 0, B, S, Hq, D, torch.bfloat16, "cuda")
+    _, _, (dq, dk, dv, _) = forward_backward(q, k, v, sink, g, W)
+    for s0, n in ((24576 - 300, 640), (S - 640, 640)):
+        a = max(0, s0 - (W - 1))
+        sl = slice(a, s0 + n)
+        rq, rk, rv, _ = oracle.attend_backward(to64(q[:, sl]), to64(k[:, sl]), to64(v[:, sl]),
+                                               to64(sink), to64(g[:, sl]), W)
+        rows = slice(s0 - a, s0 - a + n)                 # complete windows
+        check_grad(dq[:, s0:s0 + n], rq[:, rows], torch.bfloat16, "dq")
+        if s0 + n < S:
+            keys = slice(s0 - a, s0 - a + n - (W - 1))   # complete query sets
+            check_grad(dk[:, s0:s0 + n - (W - 1)], rk[:, keys], torch.bfloat16, "dk")
+            check_grad(dv[:, s0:s0 + n - (W - 1)], rv[:, keys], torch.bfloat16, "dv")
+        else:
+            # the sequence's last keys: every query that sees them is inside the slice
+            keys = slice(s0 - a, s0 - a + n)
+            check_grad(dk[:, s0:], rk[:, keys], torch.bfloat16, "dk")
+            check_grad(dv[:, s0:], rv[:, keys], torch.bfloat16, "dv")
