@@ -26,6 +26,12 @@
 //   transposing reads (A of dK^T and dV^T) are free of bank conflicts.
 //   dk/dv sum over the heads inside the wave, so no reduction across waves
 //   or work-groups is needed.
+// dk/dv ring (D = 128, windows up to 129 keys): one work-group per run of
+//   consecutive key tiles, twelve waves = six key-tile slots of an S wave and
+//   a dP wave each; the query tiles that see the run are walked once (heads
+//   innermost) and each slot takes the run's next key tile when its current
+//   one has seen its last query tile, so every Q/dO tile is staged once per
+//   run.
 #include "attn_device.h"
 #include "launch.h"
 
