@@ -72,9 +72,9 @@ struct RingSmem {
 // query head g*G + w (G = NW waves) for every 32-position step of the chunk.
 // Per step and wave the window's key tiles are processed newest first, one
 // at a time: S^T = K Q^T (MFMA), band mask on edge tiles, online softmax
-// whose running max starts at the sink s_h and is only raised when a tile
-// exceeds it by more than 2^8 (so the accumulator is almost never
-// rescaled), P packed to bf16, O^T += V^T P^T (MFMA).  The sink adds
+// whose running max starts at the sink s_h and is only raised when a tile's
+// exponentials sum past 2^8 (so every P stays <= 2^8 and the accumulator is
+// almost never rescaled), P packed to bf16, O^T += V^T P^T (MFMA).  The sink adds
 // exp(s_h - max) to the denominator once at the end.
 //
 // Per step n, each wave: passes the work-group barrier (tile T1 is whole --
@@ -248,10 +248,13 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
         }
     };
     // P = exp2(S*c - m) packed to bf16 (two K=16 operands); adds to l.
-    // The max is taken on P (canonical exp2 outputs); if some P exceeds
-    // 2^slack the running max fell behind: raise it to the tile's exact
-    // max, rescale, recompute.  A column whose max is still -inf uses an
-    // offset that sends any finite score to +inf.
+    // The check is on the lane's sum of the tile's P (a tree of adds that l
+    // needs anyway): every P is >= 0, so a sum within 2^slack bounds each
+    // of them; a larger one means the running max may have fallen behind:
+    // raise it to the tile's exact max, rescale, recompute.  (A check on
+    // the P maximum, 8 more max instructions per tile, measured 1.3% slower
+    // at 32K.)  A column whose max is still -inf uses an offset that sends
+    // any finite score to +inf.
     auto softmax_tile = [&](f32x16 &sc, float &m, float &l, f32x16 (&o)[D / 32], bf16x8 &p0b,
                             bf16x8 &p1b) {
         f32x16 p;
@@ -260,17 +263,21 @@ __global__ __launch_bounds__(NW * 64) void swa_prefill_ring_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
         }
-        float pm = fmaxf(p[0], p[1]);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) pm = fmaxf(pm, fmaxf(p[r], p[r + 1]));
-        if (__ballot(pm > kBig) != 0) {
+        auto tsum = [&]() {
+            const float a0 = p[0] + p[1], a1 = p[2] + p[3], a2 = p[4] + p[5], a3 = p[6] + p[7];
+            const float a4 = p[8] + p[9], a5 = p[10] + p[11], a6 = p[12] + p[13];
+            const float a7 = p[14] + p[15];
+            return ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7));
+        };
+        float ps = tsum();
+        if (__ballot(ps > kBig) != 0) {
             maybe_rescale(tile_max(sc), m, l, o);
             const float mu = (m == -INFINITY) ? -3.0e38f : m;
 #pragma unroll
             for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mu));
+            ps = tsum();
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) l += p[r];
+        l += ps;
         p0b = pack8(p, 0);
         p1b = pack8(p, 1);
     };
