@@ -163,10 +163,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // D_i = dO_i . O_i by packed bf16 dot products (exact products,
+            // fp32 accumulation), two elements per instruction.
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dsum_part = fmaf((float)gf[ks][e], (float)of[ks][e], dsum_part);
+            {
+                const bf16x8 a = gf[ks], o8 = of[ks];
+                dsum_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
+                                                            __builtin_shufflevector(o8, o8, 0, 1), dsum_part, false);
+                dsum_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
+                                                            __builtin_shufflevector(o8, o8, 2, 3), dsum_part, false);
+                dsum_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
+                                                            __builtin_shufflevector(o8, o8, 4, 5), dsum_part, false);
+                dsum_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
+                                                            __builtin_shufflevector(o8, o8, 6, 7), dsum_part, false);
+            }
         }
         const float l2 = lse_i * kLog2e;
         const float Di = dsum_part + __shfl_xor(dsum_part, 32);
